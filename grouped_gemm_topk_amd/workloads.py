@@ -1,0 +1,209 @@
+"""Seeded synthetic MoE-layer workloads.
+
+This module only draws numbers: it holds none of the MoE arithmetic (no
+gating, no sorting, no matrix products).  It is the single source of inputs for
+both the CPU oracle and the HIP library, so that the two are compared on exactly
+the same bits.
+
+Shapes follow the workloads described on the pages:
+
+* the fused-MoE skill card ("Fused Moe Kernel", *Key Parameters* and
+  *Small-M heuristic*) for BLOCK_M choices and small token counts;
+* the DeepSeek-V3 ~8.3B random-weight model built by the axolotl benchmark
+  scripts (``build_deepseek_v3_8b.py``, ``build_config``): H 3072, MoE
+  intermediate 2560, 18 routed experts, top-4, 6 groups / 4 kept, one shared
+  expert, ``initializer_range`` 0.02;
+* the squared-ReLU expert MLP of the mlxcel PR (fc1 -> relu^2 -> fc2);
+* decode batches of 1-3 tokens with duplicate experts across tokens, as in the
+  B70 grouped-Q8 experiment (*Intent*).
+
+Every tensor is drawn from ``numpy.random.default_rng(SeedSequence(key))`` with
+a key built from (family, tokens, layer, tensor id[, expert]), so any tensor can
+be regenerated alone.  bf16 tensors are produced as raw ``uint16`` bit
+patterns by round-to-nearest-even of a float32 draw.
+"""
+from __future__ import annotations
+
+import dataclasses
+import os
+from concurrent.futures import ThreadPoolExecutor
+from typing import Dict, Optional
+
+import numpy as np
+
+# tensor ids used in the seed keys
+_TID_X, _TID_LOGITS, _TID_W13, _TID_W2, _TID_SW13, _TID_SW2, _TID_PERM = 1, 2, 3, 4, 5, 6, 7
+
+SCORE_SOFTMAX, SCORE_SIGMOID = 0, 1
+ACT_SWIGLU, ACT_RELU2 = 0, 1
+
+
+@dataclasses.dataclass(frozen=True)
+class MoEConfig:
+    """One MoE layer shape plus the recipe of its synthetic inputs."""
+
+    name: str
+    family: int            # seed namespace (1 tiny, 2 decode, 3 DeepSeek-V3-shaped, 4 Zipf, 5 relu^2)
+    T: int
+    H: int
+    I: int
+    E: int
+    top_k: int
+    scoring: int = SCORE_SOFTMAX
+    n_group: int = 1
+    topk_group: int = 1
+    renormalize: int = 1
+    scale: float = 1.0
+    activation: int = ACT_SWIGLU
+    n_shared: int = 0
+    block_m: int = 16
+    logits_mode: str = "normal"   # "normal" | "dup3" | "zipf"
+    w_std: float = 0.02
+
+    @property
+    def M1(self) -> int:
+        """Rows of the first weight matrix per expert (2I for SwiGLU, I for relu^2)."""
+        return 2 * self.I if self.activation == ACT_SWIGLU else self.I
+
+    @property
+    def mats(self) -> int:
+        return 3 if self.activation == ACT_SWIGLU else 2
+
+    def flops(self, routed_only: bool = False) -> float:
+        """Useful flops of one layer: 2 * T * k_eff * mats * H * I (no padding)."""
+        k_eff = self.top_k + (0 if routed_only else self.n_shared)
+        return 2.0 * self.T * k_eff * self.mats * self.H * self.I
+
+
+CONFIGS: Dict[str, MoEConfig] = {
+    # tiny layer, softmax top-2 of 8, BLOCK_M 16
+    "tiny": MoEConfig("tiny", 1, T=64, H=256, I=512, E=8, top_k=2, block_m=16),
+    # decode-shaped, 128 experts top-8
+    "decode_t1": MoEConfig("decode_t1", 2, T=1, H=2048, I=768, E=128, top_k=8, block_m=16),
+    "decode_t3": MoEConfig("decode_t3", 2, T=3, H=2048, I=768, E=128, top_k=8, block_m=16,
+                           logits_mode="dup3"),
+    "decode_t8": MoEConfig("decode_t8", 2, T=8, H=2048, I=768, E=128, top_k=8, block_m=16),
+    # DeepSeek-V3-8B-shaped: grouped sigmoid routing plus one shared expert
+    "dsv3": MoEConfig("dsv3", 3, T=4096, H=3072, I=2560, E=18, top_k=4,
+                      scoring=SCORE_SIGMOID, n_group=6, topk_group=4, n_shared=1, block_m=128),
+    "dsv3_s2.5": MoEConfig("dsv3_s2.5", 3, T=4096, H=3072, I=2560, E=18, top_k=4,
+                           scoring=SCORE_SIGMOID, n_group=6, topk_group=4, n_shared=1,
+                           scale=2.5, block_m=128),
+    # 128 experts with a Zipf(1.1) popularity prior
+    "zipf128": MoEConfig("zipf128", 4, T=8192, H=2816, I=704, E=128, top_k=8, block_m=64,
+                         logits_mode="zipf"),
+    # squared-ReLU experts
+    "relu2_t1": MoEConfig("relu2_t1", 5, T=1, H=2688, I=1856, E=128, top_k=6,
+                          activation=ACT_RELU2, block_m=16),
+    "relu2_t16": MoEConfig("relu2_t16", 5, T=16, H=2688, I=1856, E=128, top_k=6,
+                           activation=ACT_RELU2, block_m=16),
+    "relu2_t2048": MoEConfig("relu2_t2048", 5, T=2048, H=2688, I=1856, E=128, top_k=6,
+                             activation=ACT_RELU2, block_m=32),
+}
+
+
+def _rng(*key: int) -> np.random.Generator:
+    return np.random.default_rng(np.random.SeedSequence([int(k) for k in key]))
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round float32 values to bf16 (nearest, ties to even); returns uint16 bits."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    b = a.view(np.uint32)
+    rounded = (b + (((b >> 16) & 1) + np.uint32(0x7FFF))) >> 16
+    return rounded.astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bit patterns to float32."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def _normal_bf16(shape, std: float, *key: int) -> np.ndarray:
+    z = _rng(*key).standard_normal(size=shape, dtype=np.float32)
+    if std != 1.0:
+        z *= np.float32(std)
+    return f32_to_bf16_bits(z)
+
+
+def _expert_stack(cfg: MoEConfig, layer: int, tid: int, rows: int, cols: int,
+                  threads: Optional[int]) -> np.ndarray:
+    """[E, rows, cols] bf16 bits, one independent stream per expert."""
+    out = np.empty((cfg.E, rows, cols), dtype=np.uint16)
+
+    def fill(e: int) -> None:
+        out[e] = _normal_bf16((rows, cols), cfg.w_std, cfg.family, layer, tid, e)
+
+    nthreads = threads or min(16, len(os.sched_getaffinity(0)))
+    if nthreads <= 1 or cfg.E == 1:
+        for e in range(cfg.E):
+            fill(e)
+    else:
+        with ThreadPoolExecutor(nthreads) as ex:
+            list(ex.map(fill, range(cfg.E)))
+    return out
+
+
+def make_logits(cfg: MoEConfig, layer: int = 0) -> np.ndarray:
+    """Router logits [T, E] float32 following the config's recipe.
+
+    * ``normal``: i.i.d. N(0, 1).
+    * ``dup3``  : three decode tokens whose preferred expert sets overlap so that
+      half of the 24 slots repeat an expert of another token.  With a seeded
+      permutation p of the experts, token 0 prefers p[0:8], token 1 prefers
+      p[0:4] + p[8:12], token 2 prefers p[4:8] + p[8:12]; preferred logits are
+      z + 6 and the others z, with z ~ N(0,1) clipped to [-2.5, 2.5] so every
+      preferred logit (>= 3.5) exceeds every other one (<= 2.5).
+    * ``zipf``  : z - 1.1 * ln(rank_e) with rank_e a seeded permutation of
+      1..E, i.e. a softmax prior proportional to rank^-1.1.
+    """
+    rng = _rng(cfg.family, cfg.T, layer, _TID_LOGITS)
+    z = rng.standard_normal(size=(cfg.T, cfg.E), dtype=np.float32)
+    if cfg.logits_mode == "normal":
+        return z
+    perm = _rng(cfg.family, cfg.T, layer, _TID_PERM).permutation(cfg.E)
+    if cfg.logits_mode == "dup3":
+        if cfg.T != 3 or cfg.top_k != 8 or cfg.E < 12:
+            raise ValueError("dup3 logits need T=3, top_k=8, E>=12")
+        z = np.clip(z, -2.5, 2.5)
+        sets = [perm[0:8], np.concatenate([perm[0:4], perm[8:12]]),
+                np.concatenate([perm[4:8], perm[8:12]])]
+        for t, s in enumerate(sets):
+            z[t, s] += np.float32(6.0)
+        return z.astype(np.float32)
+    if cfg.logits_mode == "zipf":
+        rank = (perm + 1).astype(np.float64)
+        bias = (-1.1 * np.log(rank)).astype(np.float32)
+        return (z + bias[None, :]).astype(np.float32)
+    raise ValueError(f"unknown logits_mode {cfg.logits_mode!r}")
+
+
+def make_inputs(cfg: MoEConfig, layer: int = 0, with_weights: bool = True,
+                threads: Optional[int] = None) -> Dict[str, np.ndarray]:
+    """All inputs of one layer as numpy arrays.
+
+    Returns ``x`` (uint16 bf16 bits [T,H]), ``logits`` (float32 [T,E]) and, with
+    ``with_weights``, ``w13`` (bf16 bits [E,M1,H]; SwiGLU rows [0,I) gate,
+    [I,2I) up), ``w2`` (bf16 bits [E,H,I]) and, when ``n_shared`` is 1,
+    ``shared_w13`` ([M1,H]) and ``shared_w2`` ([H,I]).
+    """
+    inp: Dict[str, np.ndarray] = {
+        "x": _normal_bf16((cfg.T, cfg.H), 1.0, cfg.family, cfg.T, layer, _TID_X),
+        "logits": make_logits(cfg, layer),
+    }
+    if with_weights:
+        inp["w13"] = _expert_stack(cfg, layer, _TID_W13, cfg.M1, cfg.H, threads)
+        inp["w2"] = _expert_stack(cfg, layer, _TID_W2, cfg.H, cfg.I, threads)
+        if cfg.n_shared:
+            inp["shared_w13"] = _normal_bf16((cfg.M1, cfg.H), cfg.w_std, cfg.family, layer,
+                                             _TID_SW13)
+            inp["shared_w2"] = _normal_bf16((cfg.H, cfg.I), cfg.w_std, cfg.family, layer,
+                                            _TID_SW2)
+    return inp
+
+
+def small_config(name: str = "small", **kw) -> MoEConfig:
+    """A config for oracle-sized parity cases; keyword arguments override fields."""
+    base = dict(name=name, family=100, T=37, H=64, I=96, E=8, top_k=2, block_m=16)
+    base.update(kw)
+    return MoEConfig(**base)
