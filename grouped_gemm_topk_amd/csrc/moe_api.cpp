@@ -1,0 +1,367 @@
+// libmoe C ABI: argument validation, workspace layout and kernel dispatch.
+//
+// Every check runs on the host before anything is enqueued, so an invalid call
+// writes nothing.  The library never allocates, synchronises or copies to the
+// host; the only state it keeps is a per-device cache of "is this a gfx950".
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstring>
+
+#include "../../include/moe.h"
+#include "moe_internal.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_dev_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP_BASE - (int)e; }
+
+int check_device() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_DEVICE;
+  int st = g_dev_state[dev].load(std::memory_order_acquire);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return hip_status(e);
+    st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_dev_state[dev].store(st, std::memory_order_release);
+  }
+  return st == 1 ? MOE_OK : MOE_ERR_DEVICE;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+bool valid_bm(int bm) { return bm == 16 || bm == 32 || bm == 64 || bm == 128; }
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+int align_nblocks(int64_t n) { return (int)((n + moe::kAlignChunk - 1) / moe::kAlignChunk); }
+
+// scratch of the multi-block align: per-chunk histograms + expert offsets
+size_t align_scratch_bytes(int64_t n, int E) {
+  if (n <= moe::kSingleBlockSlots) return 0;
+  return round_up((size_t)(align_nblocks(n) + 1) * E * sizeof(int), 256);
+}
+
+// Carves a workspace into 256-byte aligned regions.
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base((char*)b) {}
+  void* take(size_t bytes) {
+    void* p = base ? base + off : nullptr;
+    off += round_up(bytes, 256);
+    return p;
+  }
+};
+
+int validate_layer(const moe_layer_params* p) {
+  if (!p) return MOE_ERR_NULL;
+  if (p->T < 0 || p->H <= 0 || p->I <= 0) return MOE_ERR_SHAPE;
+  if (p->H % 8 != 0 || p->I % 8 != 0) return MOE_ERR_SHAPE;
+  if (p->E < 1 || p->E > MOE_MAX_EXPERTS) return MOE_ERR_SHAPE;
+  if (p->top_k < 1 || p->top_k > MOE_MAX_TOPK || p->top_k > p->E) return MOE_ERR_SHAPE;
+  if (!valid_bm(p->block_m)) return MOE_ERR_SHAPE;
+  if (p->scoring != MOE_SCORE_SOFTMAX && p->scoring != MOE_SCORE_SIGMOID) return MOE_ERR_SHAPE;
+  if (p->n_group < 1 || p->n_group > 64 || p->E % p->n_group != 0) return MOE_ERR_SHAPE;
+  if (p->topk_group < 1 || p->topk_group > p->n_group) return MOE_ERR_SHAPE;
+  if ((int64_t)p->topk_group * (p->E / p->n_group) < p->top_k) return MOE_ERR_SHAPE;
+  if (p->n_group > 1 && p->scoring != MOE_SCORE_SIGMOID) return MOE_ERR_UNSUPPORTED;
+  if (p->renormalize != 0 && p->renormalize != 1) return MOE_ERR_SHAPE;
+  if (!std::isfinite(p->routed_scaling_factor)) return MOE_ERR_SHAPE;
+  if (p->activation != MOE_ACT_SWIGLU && p->activation != MOE_ACT_RELU2) return MOE_ERR_SHAPE;
+  if (p->n_shared != 0 && p->n_shared != 1) return MOE_ERR_SHAPE;
+  if ((int64_t)p->T * p->top_k > (1 << 28)) return MOE_ERR_SHAPE;
+  if ((int64_t)p->T * p->H > ((int64_t)1 << 40)) return MOE_ERR_SHAPE;
+  return MOE_OK;
+}
+
+struct LayerWorkspace {
+  int32_t* topk_ids;
+  float* topk_w;
+  int32_t* sorted;
+  int32_t* expert_ids;
+  int32_t* ntpp;
+  int32_t* align_scratch;
+  uint16_t* act;      // [cap, I] bf16 in padded order
+  uint16_t* act_sh;   // [T, I] bf16, shared expert
+  float* yslot;       // [T*k (+T), H] fp32 weighted expert outputs
+  size_t bytes;
+};
+
+LayerWorkspace layout_layer(const moe_layer_params* p, void* ws) {
+  const int64_t n = (int64_t)p->T * p->top_k;
+  const int64_t cap = MOE_ALIGN_CAPACITY(p->T, p->top_k, p->E, p->block_m);
+  Carver c(ws);
+  LayerWorkspace w;
+  w.topk_ids = (int32_t*)c.take(n * 4);
+  w.topk_w = (float*)c.take(n * 4);
+  w.sorted = (int32_t*)c.take(cap * 4);
+  w.expert_ids = (int32_t*)c.take(cap / p->block_m * 4);
+  w.ntpp = (int32_t*)c.take(4);
+  w.align_scratch = (int32_t*)c.take(align_scratch_bytes(n, p->E));
+  w.act = (uint16_t*)c.take((size_t)cap * p->I * 2);
+  w.act_sh = (uint16_t*)c.take((size_t)(p->n_shared ? p->T : 0) * p->I * 2);
+  w.yslot = (float*)c.take((size_t)(n + (p->n_shared ? p->T : 0)) * p->H * 4);
+  w.bytes = c.off;
+  return w;
+}
+
+moe::AlignParams make_align(const int32_t* ids, int64_t n, int E, int bm, int32_t* sorted,
+                            int32_t* expert_ids, int32_t* ntpp, int32_t* scratch) {
+  moe::AlignParams a{};
+  a.topk_ids = ids;
+  a.n = (int)n;
+  a.E = E;
+  a.block_m = bm;
+  a.sorted_ids = sorted;
+  a.expert_ids = expert_ids;
+  a.ntpp = ntpp;
+  a.nblocks = align_nblocks(n);
+  a.block_counts = scratch;
+  a.expert_off = scratch ? scratch + (int64_t)a.nblocks * E : nullptr;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t moe_align_capacity(int32_t T, int32_t k, int32_t E, int32_t block_m) {
+  if (T < 0 || k < 1 || E < 1 || !valid_bm(block_m)) return -1;
+  return MOE_ALIGN_CAPACITY(T, k, E, block_m);
+}
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "a size is out of range or inconsistent";
+    case MOE_ERR_CAPACITY: return "an output buffer or the workspace is too small";
+    case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MOE_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case MOE_ERR_DEVICE: return "the current device is not a gfx950 GPU";
+    default: return status <= MOE_ERR_HIP_BASE ? "HIP runtime error" : "unknown status";
+  }
+}
+
+int moe_align(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E, int32_t block_m,
+              int32_t* sorted_token_ids, int32_t* expert_ids, int32_t* num_tokens_post_padded,
+              int64_t capacity, void* workspace, size_t* workspace_bytes, void* stream) {
+  if (!workspace_bytes) return MOE_ERR_NULL;
+  if (T < 0 || k < 1 || k > MOE_MAX_TOPK || E < 1 || E > MOE_MAX_EXPERTS || k > E)
+    return MOE_ERR_SHAPE;
+  if (!valid_bm(block_m)) return MOE_ERR_SHAPE;
+  const int64_t n = (int64_t)T * k;
+  if (n > (1 << 28)) return MOE_ERR_SHAPE;
+  const size_t need = align_scratch_bytes(n, E);
+  if (!workspace && need > 0) {
+    *workspace_bytes = need;
+    return MOE_OK;
+  }
+  if (!workspace) *workspace_bytes = 0;
+  if (!sorted_token_ids || !expert_ids || !num_tokens_post_padded) return MOE_ERR_NULL;
+  if (n > 0 && !topk_ids) return MOE_ERR_NULL;
+  if (capacity < MOE_ALIGN_CAPACITY(T, k, E, block_m)) return MOE_ERR_CAPACITY;
+  if (workspace && *workspace_bytes < need) return MOE_ERR_CAPACITY;
+  if (!aligned4(topk_ids) || !aligned4(sorted_token_ids) || !aligned4(expert_ids) ||
+      !aligned4(num_tokens_post_padded) || !aligned16(workspace))
+    return MOE_ERR_ALIGN;
+  int st = check_device();
+  if (st != MOE_OK) return st;
+  moe::AlignParams a = make_align(topk_ids, n, E, block_m, sorted_token_ids, expert_ids,
+                                  num_tokens_post_padded, (int32_t*)workspace);
+  return hip_status(moe::launch_align(a, (hipStream_t)stream));
+}
+
+int moe_grouped_gemm(const moe_gemm_args* args, void* workspace, size_t* workspace_bytes,
+                     void* stream) {
+  (void)workspace;
+  if (!args || !workspace_bytes) return MOE_ERR_NULL;
+  const moe_gemm_args& g = *args;
+  if (g.E < 1 || g.E > MOE_MAX_EXPERTS || g.N <= 0 || g.K <= 0) return MOE_ERR_SHAPE;
+  if (g.K % 8 != 0 || g.N % 8 != 0) return MOE_ERR_SHAPE;
+  if (g.epilogue < MOE_EPI_STORE || g.epilogue > MOE_EPI_WEIGHTED_SCATTER) return MOE_ERR_SHAPE;
+  if (g.epilogue == MOE_EPI_SWIGLU && g.N % 16 != 0) return MOE_ERR_SHAPE;
+  if (!valid_bm(g.block_m)) return MOE_ERR_SHAPE;
+  if (g.capacity < 0 || g.capacity % g.block_m != 0) return MOE_ERR_SHAPE;
+  if (g.num_valid < 0 || g.a_row_div < 0) return MOE_ERR_SHAPE;
+  if (g.a_row_div > 0 && g.num_valid % g.a_row_div != 0) return MOE_ERR_SHAPE;
+  if (g.c_is_fp32 != 0 && g.c_is_fp32 != 1) return MOE_ERR_SHAPE;
+  *workspace_bytes = 0;   // this call needs no workspace and always runs
+  if (g.capacity == 0) return MOE_OK;
+  if (!g.a || !g.w || !g.c || !g.sorted_token_ids || !g.expert_ids || !g.num_tokens_post_padded)
+    return MOE_ERR_NULL;
+  if (g.epilogue == MOE_EPI_WEIGHTED_SCATTER && !g.topk_weights) return MOE_ERR_NULL;
+  if (!aligned16(g.a) || !aligned16(g.w) || !aligned16(g.c)) return MOE_ERR_ALIGN;
+  int st = check_device();
+  if (st != MOE_OK) return st;
+  moe::GemmParams p{};
+  p.A = (const uint16_t*)g.a;
+  p.a_row_div = g.a_row_div;
+  p.W = (const uint16_t*)g.w;
+  p.E = g.E;
+  p.N = g.N;
+  p.K = g.K;
+  p.I = g.epilogue == MOE_EPI_SWIGLU ? g.N / 2 : g.N;
+  p.sorted_ids = g.sorted_token_ids;
+  p.expert_ids = g.expert_ids;
+  p.ntpp = g.num_tokens_post_padded;
+  p.M = g.capacity;
+  p.num_valid = g.num_valid;
+  p.epi = g.epilogue;
+  p.topk_w = g.topk_weights;
+  p.C = g.c;
+  p.c_fp32 = g.c_is_fp32;
+  p.c_row_offset = 0;
+  p.ldc = g.epilogue == MOE_EPI_SWIGLU ? g.N / 2 : g.N;
+  return hip_status(moe::launch_grouped_gemm(p, g.block_m, (hipStream_t)stream));
+}
+
+int moe_fused_forward(const moe_layer_params* p, const void* x, const float* router_logits,
+                      const void* w13, const void* w2, const void* shared_w13,
+                      const void* shared_w2, float* out, int32_t* topk_ids, float* topk_weights,
+                      int32_t* sorted_token_ids, int32_t* expert_ids,
+                      int32_t* num_tokens_post_padded, void* workspace, size_t* workspace_bytes,
+                      void* stream) {
+  if (!workspace_bytes) return MOE_ERR_NULL;
+  int st = validate_layer(p);
+  if (st != MOE_OK) return st;
+  LayerWorkspace L = layout_layer(p, nullptr);
+  if (!workspace) {
+    *workspace_bytes = L.bytes;
+    return MOE_OK;
+  }
+  if (*workspace_bytes < L.bytes) return MOE_ERR_CAPACITY;
+  if (p->T == 0) return MOE_OK;
+  if (!x || !router_logits || !w13 || !w2 || !out) return MOE_ERR_NULL;
+  if (p->n_shared && (!shared_w13 || !shared_w2)) return MOE_ERR_NULL;
+  if (!aligned16(x) || !aligned16(w13) || !aligned16(w2) || !aligned16(out) ||
+      !aligned16(workspace) || !aligned4(router_logits) ||
+      (p->n_shared && (!aligned16(shared_w13) || !aligned16(shared_w2))) ||
+      !aligned4(topk_ids) || !aligned4(topk_weights) || !aligned4(sorted_token_ids) ||
+      !aligned4(expert_ids) || !aligned4(num_tokens_post_padded))
+    return MOE_ERR_ALIGN;
+  st = check_device();
+  if (st != MOE_OK) return st;
+
+  hipStream_t s = (hipStream_t)stream;
+  L = layout_layer(p, workspace);
+  const int T = p->T, H = p->H, I = p->I, E = p->E, k = p->top_k, bm = p->block_m;
+  const int64_t n = (int64_t)T * k;
+  const int64_t cap = MOE_ALIGN_CAPACITY(T, k, E, bm);
+  const int M1 = p->activation == MOE_ACT_SWIGLU ? 2 * I : I;
+
+  int32_t* ids = topk_ids ? topk_ids : L.topk_ids;
+  float* wts = topk_weights ? topk_weights : L.topk_w;
+  int32_t* sorted = sorted_token_ids ? sorted_token_ids : L.sorted;
+  int32_t* eids = expert_ids ? expert_ids : L.expert_ids;
+  int32_t* ntpp = num_tokens_post_padded ? num_tokens_post_padded : L.ntpp;
+
+  // ---- routing
+  moe::GateParams g{};
+  g.logits = router_logits;
+  g.T = T;
+  g.E = E;
+  g.k = k;
+  g.scoring = p->scoring;
+  g.n_group = p->n_group;
+  g.topk_group = p->topk_group;
+  g.renorm = p->renormalize;
+  g.scale = p->routed_scaling_factor;
+  g.topk_ids = ids;
+  g.topk_w = wts;
+  moe::AlignParams a = make_align(ids, n, E, bm, sorted, eids, ntpp, L.align_scratch);
+  hipError_t e;
+  if (T <= moe::kRouteFusedTokens && n <= moe::kSingleBlockSlots) {
+    e = moe::launch_route_fused(g, a, s);
+  } else {
+    e = moe::launch_gate(g, s);
+    if (e == hipSuccess) e = moe::launch_align(a, s);
+  }
+  if (e != hipSuccess) return hip_status(e);
+
+  // ---- GEMM1 + activation: act[i] = act(x[sorted[i] / k] . w13[e]^T)
+  const int epi1 = p->activation == MOE_ACT_SWIGLU ? MOE_EPI_SWIGLU : MOE_EPI_RELU2;
+  moe::GemmParams g1{};
+  g1.A = (const uint16_t*)x;
+  g1.a_row_div = k;
+  g1.W = (const uint16_t*)w13;
+  g1.E = E;
+  g1.N = M1;
+  g1.K = H;
+  g1.I = I;
+  g1.sorted_ids = sorted;
+  g1.expert_ids = eids;
+  g1.ntpp = ntpp;
+  g1.M = (int)cap;
+  g1.num_valid = (int)n;
+  g1.epi = epi1;
+  g1.C = L.act;
+  g1.c_fp32 = 0;
+  g1.ldc = I;
+  e = moe::launch_grouped_gemm(g1, bm, s);
+  if (e != hipSuccess) return hip_status(e);
+  if (p->n_shared) {
+    moe::GemmParams gs = g1;
+    gs.W = (const uint16_t*)shared_w13;
+    gs.E = 1;
+    gs.a_row_div = 0;
+    gs.sorted_ids = nullptr;
+    gs.expert_ids = nullptr;
+    gs.ntpp = nullptr;
+    gs.M = T;
+    gs.C = L.act_sh;
+    e = moe::launch_grouped_gemm(gs, bm, s);
+    if (e != hipSuccess) return hip_status(e);
+  }
+
+  // ---- GEMM2 + routed weight, scattered to slot rows of yslot
+  moe::GemmParams g2{};
+  g2.A = L.act;
+  g2.a_row_div = 0;
+  g2.W = (const uint16_t*)w2;
+  g2.E = E;
+  g2.N = H;
+  g2.K = I;
+  g2.I = H;
+  g2.sorted_ids = sorted;
+  g2.expert_ids = eids;
+  g2.ntpp = ntpp;
+  g2.M = (int)cap;
+  g2.num_valid = (int)n;
+  g2.epi = MOE_EPI_WEIGHTED_SCATTER;
+  g2.topk_w = wts;
+  g2.C = L.yslot;
+  g2.c_fp32 = 1;
+  g2.c_row_offset = 0;
+  g2.ldc = H;
+  e = moe::launch_grouped_gemm(g2, bm, s);
+  if (e != hipSuccess) return hip_status(e);
+  if (p->n_shared) {
+    moe::GemmParams gs = g2;
+    gs.A = L.act_sh;
+    gs.W = (const uint16_t*)shared_w2;
+    gs.E = 1;
+    gs.sorted_ids = nullptr;
+    gs.expert_ids = nullptr;
+    gs.ntpp = nullptr;
+    gs.M = T;
+    gs.topk_w = nullptr;
+    gs.c_row_offset = n;
+    e = moe::launch_grouped_gemm(gs, bm, s);
+    if (e != hipSuccess) return hip_status(e);
+  }
+
+  // ---- combine
+  e = moe::launch_combine(L.yslot, T, k, H, p->n_shared, out, s);
+  return hip_status(e);
+}
+
+}  // extern "C"

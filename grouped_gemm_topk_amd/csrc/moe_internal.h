@@ -1,0 +1,68 @@
+// Internal declarations of libmoe: kernel parameter blocks and launchers.
+// Host code (moe_api.cpp) validates arguments and carves the workspace; the
+// .hip files own the kernels and expose one launcher per kernel family.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---------------------------------------------------------------- gating
+struct GateParams {
+  const float* logits;  // [T, E]
+  int T, E, k;
+  int scoring;          // 0 softmax, 1 sigmoid
+  int n_group, topk_group;
+  int renorm;
+  float scale;
+  int* topk_ids;        // [T, k]
+  float* topk_w;        // [T, k]
+};
+
+// ---------------------------------------------------------------- align
+struct AlignParams {
+  const int* topk_ids;  // [n]
+  int n;                // T * k
+  int E;
+  int block_m;
+  int* sorted_ids;      // [capacity]
+  int* expert_ids;      // [capacity / block_m]
+  int* ntpp;            // [1]
+  int* block_counts;    // workspace [nblocks, E] (multi-block path)
+  int* expert_off;      // workspace [E]          (multi-block path)
+  int nblocks;          // chunks of kAlignChunk slots
+};
+
+constexpr int kAlignChunk = 4096;      // slots per workgroup in the multi-block path
+constexpr int kSingleBlockSlots = 4096; // at most this many slots: one workgroup does it all
+constexpr int kRouteFusedTokens = 64;   // gating fused into the one-workgroup align up to this T
+
+// ---------------------------------------------------------------- grouped GEMM
+struct GemmParams {
+  const uint16_t* A;        // bf16 rows of K elements
+  int a_row_div;            // >0: A row = sid / a_row_div; 0: A row = padded position
+  const uint16_t* W;        // bf16 [E, N, K] (or one matrix when expert_ids is null)
+  int E, N, K;
+  int I;                    // SwiGLU: act columns (= N / 2); else N
+  const int* sorted_ids;    // null: dense rows (row i is A row i, valid when i < M)
+  const int* expert_ids;    // null: expert 0
+  const int* ntpp;          // null: M rows in total
+  int M;                    // dense mode: number of rows; routed: capacity
+  int num_valid;            // pad threshold of sorted ids
+  int epi;                  // 0 store, 1 swiglu, 2 relu2, 3 weighted scatter
+  const float* topk_w;      // weighted scatter: routed weight per slot (null: 1)
+  void* C;
+  int c_fp32;
+  int64_t c_row_offset;     // weighted scatter: added to the destination row
+  int ldc;                  // output row stride in elements
+};
+
+hipError_t launch_gate(const GateParams& p, hipStream_t s);
+hipError_t launch_route_fused(const GateParams& g, const AlignParams& a, hipStream_t s);
+hipError_t launch_align(const AlignParams& p, hipStream_t s);
+hipError_t launch_grouped_gemm(const GemmParams& p, int block_m, hipStream_t s);
+hipError_t launch_combine(const float* yslot, int T, int k, int H, int has_shared, float* out,
+                          hipStream_t s);
+
+}  // namespace moe

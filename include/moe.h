@@ -1,0 +1,188 @@
+/*
+ * libmoe — fused Mixture-of-Experts forward for AMD Instinct MI355X (gfx950).
+ *
+ * The problem statement follows the fused-MoE recipe of the "Fused Moe Kernel"
+ * skill card (zjli2013/fused-moe-kernel), sections *Token-Expert Routing*,
+ * *Grouped GEMM Structure* and *Common Pitfalls*: top-k gating, sorting the
+ * token slots by expert with every expert padded to a multiple of BLOCK_M,
+ * then a tiled grouped GEMM that reaches its token rows through
+ * `sorted_token_ids` and its weight matrix through `expert_ids`, skipping
+ * blocks at or beyond `num_tokens_post_padded`.  The expert MLP is SwiGLU
+ * (`act_fn(gate) * up`, the axolotl DeepSeek-V3 MoE forward) or squared ReLU
+ * (fc1 -> relu^2 -> fc2, mlxcel PR #280).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Tensor pointers are DEVICE pointers, row-major with the innermost
+ *   dimension contiguous, 16-byte aligned.  bf16 tensors are raw uint16 bit
+ *   patterns.  `stream` is a hipStream_t (NULL = the default stream).
+ * - The caller owns every buffer, including the workspace.  The library never
+ *   allocates device memory, never synchronises the stream and never copies to
+ *   the host.  All work is enqueued asynchronously on `stream`.
+ * - Workspace: `workspace_bytes` must not be NULL.  When a call needs a
+ *   workspace and `workspace == NULL`, the required byte count is written to
+ *   `*workspace_bytes` and nothing is launched; call again with a buffer of at
+ *   least that many bytes and its size in `*workspace_bytes`.  A call that
+ *   needs none (required size 0) writes 0 to `*workspace_bytes` and runs.
+ * - Arguments are validated on the host before anything is launched; a
+ *   negative status is returned and nothing is written.  There is no fallback
+ *   path: an unsupported case is an error.  HIP failures are returned as
+ *   MOE_ERR_HIP_BASE - (int)hipError_t.
+ * - Slot s = t * top_k + j indexes the routing of token t to its j-th expert;
+ *   num_valid = T * top_k.  Pad entries of `sorted_token_ids` equal num_valid.
+ * - Calls on one stream are ordered; calls on different streams that share
+ *   output or workspace buffers race.
+ */
+#ifndef LIBMOE_MOE_H
+#define LIBMOE_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL = -1,         /* a required pointer is NULL                        */
+  MOE_ERR_SHAPE = -2,        /* a size is out of range or inconsistent            */
+  MOE_ERR_CAPACITY = -3,     /* an output or the workspace is too small           */
+  MOE_ERR_UNSUPPORTED = -4,  /* valid request this build does not implement       */
+  MOE_ERR_ALIGN = -5,        /* a pointer is not 16-byte aligned                  */
+  MOE_ERR_DEVICE = -6,       /* the current device is not a gfx950 GPU            */
+  MOE_ERR_HIP_BASE = -1000
+} moe_status;
+
+enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 };
+enum { MOE_ACT_SWIGLU = 0, MOE_ACT_RELU2 = 1 };
+enum { MOE_EPI_STORE = 0, MOE_EPI_SWIGLU = 1, MOE_EPI_RELU2 = 2, MOE_EPI_WEIGHTED_SCATTER = 3 };
+
+/* Limits enforced by validation. */
+#define MOE_MAX_EXPERTS 256
+#define MOE_MAX_TOPK 16
+
+/* Padded-length bound of moe_align: round_up(T*k + min(E, T*k) * (bm - 1), bm).
+ * Every expert wastes at most bm - 1 pad slots and at most min(E, T*k) experts
+ * are non-empty. */
+#define MOE_ALIGN_CAPACITY(T, k, E, bm)                                              \
+  ((((int64_t)(T) * (k) + ((int64_t)(E) < (int64_t)(T) * (k) ? (int64_t)(E)        \
+                                                             : (int64_t)(T) * (k)) * \
+         ((bm) - 1)) + (bm) - 1) / (bm) * (bm))
+
+/* Same bound as a function (for bindings that cannot expand macros). */
+int64_t moe_align_capacity(int32_t T, int32_t k, int32_t E, int32_t block_m);
+
+/*
+ * moe_align — sort token slots by expert and pad every expert to a multiple of
+ * block_m (skill card, *Token-Expert Routing* steps 2-3; the sorted-id /
+ * expert-id / padded-count triple of *Grouped GEMM Structure*).
+ *
+ *   topk_ids                int32 [T, k]   expert of each slot, 0 <= id < E
+ *   block_m                 16, 32, 64 or 128
+ *   sorted_token_ids  (out) int32 [capacity]: for expert e with c_e slots, its
+ *                           padded range [o_e, o_e + p_e) (p_e = ceil(c_e/bm)*bm,
+ *                           0 when c_e = 0; o_e = sum of p over lower experts)
+ *                           holds the expert's slots in ascending order, then
+ *                           num_valid for the pads.
+ *   expert_ids        (out) int32 [capacity / block_m]: expert of each block.
+ *   num_tokens_post_padded (out) int32 [1]: sum of p_e.
+ *   capacity                entries of sorted_token_ids; must be at least
+ *                           MOE_ALIGN_CAPACITY(T, k, E, block_m).
+ * Entries at or beyond num_tokens_post_padded (or its block count) are left
+ * unspecified.  Ids outside [0, E) are an error of the caller (they are
+ * dropped and the output is then unspecified).  T = 0 writes 0 to
+ * num_tokens_post_padded.
+ */
+int moe_align(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E, int32_t block_m,
+              int32_t* sorted_token_ids, int32_t* expert_ids,
+              int32_t* num_tokens_post_padded, int64_t capacity, void* workspace,
+              size_t* workspace_bytes, void* stream);
+
+/*
+ * One grouped GEMM over the aligned layout (skill card, *Grouped GEMM
+ * Structure*; expert weights stacked [E, N, K], *Common Pitfalls* 3):
+ *
+ *   for padded row i < num_tokens_post_padded, e = expert_ids[i / block_m],
+ *   s = sorted_token_ids[i], a = A[s / a_row_div] (a_row_div > 0) or A[i]
+ *   (a_row_div == 0), h = a . W[e]^T (fp32 accumulation) and
+ *     STORE            C[i] = h                                   (N columns)
+ *     SWIGLU           C[i] = silu(h[:N/2]) * h[N/2:]             (N/2 columns)
+ *     RELU2            C[i] = max(h, 0)^2                         (N columns)
+ *     WEIGHTED_SCATTER C[s] = topk_weights[s] * h, only if s < num_valid
+ *   Row-ordered epilogues (STORE/SWIGLU/RELU2) write zero rows for pads.
+ */
+typedef struct {
+  const void* a;           /* bf16 A rows, row stride K                                  */
+  int32_t a_row_div;       /* top_k to gather token rows of x; 0 = A in padded order     */
+  const void* w;           /* bf16 [E, N, K]                                             */
+  int32_t E, N, K;         /* K multiple of 8; N multiple of 8 (of 16 for SWIGLU)        */
+  const int32_t* sorted_token_ids;        /* from moe_align                              */
+  const int32_t* expert_ids;              /* from moe_align                              */
+  const int32_t* num_tokens_post_padded;  /* device scalar from moe_align                */
+  int32_t block_m;         /* the block_m moe_align used                                 */
+  int32_t num_valid;       /* T * top_k                                                  */
+  int32_t capacity;        /* entries of sorted_token_ids (multiple of block_m)          */
+  int32_t epilogue;        /* MOE_EPI_*                                                  */
+  const float* topk_weights; /* [num_valid] for WEIGHTED_SCATTER                         */
+  void* c;                 /* output rows: capacity rows (row-ordered) or num_valid rows */
+  int32_t c_is_fp32;       /* 1: fp32 output, 0: bf16 (round to nearest even)            */
+} moe_gemm_args;
+
+int moe_grouped_gemm(const moe_gemm_args* args, void* workspace, size_t* workspace_bytes,
+                     void* stream);
+
+/*
+ * The whole routed MoE layer: gating -> align -> GEMM1 + activation ->
+ * GEMM2 + routed weight -> combine (the axolotl DeepSeek-V3 MoE forward
+ * `_moe_triton_forward`, fused; the skill card's recipe end to end).
+ */
+typedef struct {
+  int32_t T, H, I, E, top_k;
+  int32_t block_m;        /* 16, 32, 64 or 128                                            */
+  int32_t scoring;        /* MOE_SCORE_SOFTMAX or MOE_SCORE_SIGMOID                       */
+  int32_t n_group;        /* expert groups (1 = no grouping); E % n_group == 0            */
+  int32_t topk_group;     /* groups kept per token                                        */
+  int32_t renormalize;    /* 1: weights sum to 1 over the selected experts                */
+  float routed_scaling_factor; /* multiplies the routed weights (1.0 = none)              */
+  int32_t activation;     /* MOE_ACT_SWIGLU or MOE_ACT_RELU2                              */
+  int32_t n_shared;       /* 0 or 1 always-on shared expert, weight 1                     */
+} moe_layer_params;
+
+/*
+ * Gating (per token; ties broken toward the lower expert index):
+ *   softmax scoring: experts ranked by logit; weight_j = exp(l_j - m) / sum over
+ *     the selected set (renormalize) or over all experts; times the scale.
+ *   sigmoid scoring: with n_group > 1, groups of E/n_group contiguous experts
+ *     are ranked by the sum of their two largest sigmoids (fp64) and only the
+ *     best topk_group groups stay candidates; experts ranked by logit; weight_j =
+ *     sigmoid_j / sum over the selected set (renormalize) or sigmoid_j; times
+ *     the scale.
+ *
+ *   x             bf16 [T, H]
+ *   router_logits fp32 [T, E] (finite)
+ *   w13           bf16 [E, M1, H]; SwiGLU: M1 = 2I, rows [0,I) gate, [I,2I) up;
+ *                 relu^2: M1 = I
+ *   w2            bf16 [E, H, I]
+ *   shared_w13    bf16 [M1, H] and shared_w2 bf16 [H, I] when n_shared = 1
+ *   out     (out) fp32 [T, H]
+ *   topk_ids, topk_weights (optional out) int32 / fp32 [T, top_k]
+ *   sorted_token_ids, expert_ids, num_tokens_post_padded (optional out): as
+ *     moe_align, sized for MOE_ALIGN_CAPACITY(T, top_k, E, block_m)
+ * Limits: 1 <= E <= 256, 1 <= top_k <= min(E, 16), H and I multiples of 8,
+ * topk_group * E / n_group >= top_k.  T = 0 returns MOE_OK with nothing launched.
+ */
+int moe_fused_forward(const moe_layer_params* p, const void* x, const float* router_logits,
+                      const void* w13, const void* w2, const void* shared_w13,
+                      const void* shared_w2, float* out, int32_t* topk_ids,
+                      float* topk_weights, int32_t* sorted_token_ids, int32_t* expert_ids,
+                      int32_t* num_tokens_post_padded, void* workspace,
+                      size_t* workspace_bytes, void* stream);
+
+/* Human-readable text of a status code (static storage). */
+const char* moe_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LIBMOE_MOE_H */

@@ -1,0 +1,151 @@
+"""The C ABI without a GPU: the library loads, exports every declared entry
+point, and rejects invalid arguments on the host before touching a device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from grouped_gemm_topk_amd import moe as M
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|int64_t|const char\s*\*)\s+(moe_\w+)\s*\(", src,
+                                 flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(M.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return M.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared()
+    assert set(names) >= {"moe_align", "moe_grouped_gemm", "moe_fused_forward"}
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(M.EXPORTED) <= set(names)
+
+
+def test_capacity_matches_macro(L):
+    for T, k, E, bm in [(1, 8, 128, 16), (4096, 4, 18, 128), (8192, 8, 128, 64), (0, 2, 8, 16),
+                        (3, 2, 64, 32)]:
+        n = T * k
+        want = (n + min(E, n) * (bm - 1) + bm - 1) // bm * bm
+        assert L.moe_align_capacity(T, k, E, bm) == want
+    assert L.moe_align_capacity(1, 1, 1, 24) == -1
+
+
+def _layer(**kw):
+    base = dict(T=4, H=64, I=32, E=8, top_k=2, block_m=16)
+    base.update(kw)
+    return M.LayerParams(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=-1), -2), (dict(H=60), -2), (dict(I=12), -2), (dict(E=0), -2), (dict(E=257), -2),
+    (dict(top_k=0), -2), (dict(top_k=9), -2), (dict(top_k=17, E=32), -2), (dict(block_m=24), -2),
+    (dict(scoring=2), -2), (dict(n_group=3), -2), (dict(n_group=4, topk_group=5), -2),
+    (dict(n_group=4, topk_group=1, top_k=3, scoring=1), -2),
+    (dict(n_group=2, topk_group=1), -4), (dict(activation=3), -2), (dict(n_shared=2), -2),
+    (dict(renormalize=2), -2), (dict(routed_scaling_factor=float("inf")), -2),
+])
+def test_fused_forward_rejects_bad_params(L, kw, status):
+    p = _layer(**kw).c_struct()
+    n = ctypes.c_size_t(0)
+    st = L.moe_fused_forward(ctypes.byref(p), None, None, None, None, None, None, None, None, None,
+                             None, None, None, None, ctypes.byref(n), None)
+    assert st == status
+    assert n.value == 0
+
+
+def test_fused_forward_size_query_and_null_checks(L):
+    p = _layer().c_struct()
+    n = ctypes.c_size_t(0)
+    assert L.moe_fused_forward(ctypes.byref(p), *([None] * 13), ctypes.byref(n), None) == 0
+    assert n.value > 0
+    need = n.value
+    fake = 1 << 20     # never dereferenced: validation fails first
+    small = ctypes.c_size_t(need - 1)
+    assert L.moe_fused_forward(ctypes.byref(p), *([fake] * 12), fake, ctypes.byref(small),
+                               None) == -3
+    ok = ctypes.c_size_t(need)
+    args = [fake] * 13
+    args[0] = None   # x missing
+    assert L.moe_fused_forward(ctypes.byref(p), *args, ctypes.byref(ok), None) == -1
+    args = [fake] * 13
+    args[0] = fake + 2   # misaligned x
+    assert L.moe_fused_forward(ctypes.byref(p), *args, ctypes.byref(ok), None) == -5
+    p2 = _layer(n_shared=1).c_struct()
+    n2 = ctypes.c_size_t(0)
+    L.moe_fused_forward(ctypes.byref(p2), *([None] * 13), ctypes.byref(n2), None)
+    assert n2.value > need
+    args = [fake] * 13
+    args[4] = None   # shared_w13 missing
+    assert L.moe_fused_forward(ctypes.byref(p2), *args, ctypes.byref(n2), None) == -1
+    assert L.moe_fused_forward(ctypes.byref(p), *([fake] * 13), None, None) == -1
+
+
+def test_fused_forward_t0_is_noop(L):
+    p = _layer(T=0).c_struct()
+    n = ctypes.c_size_t(0)
+    assert L.moe_fused_forward(ctypes.byref(p), *([None] * 13), ctypes.byref(n), None) == 0
+    ws = ctypes.c_size_t(n.value)
+    assert L.moe_fused_forward(ctypes.byref(p), *([None] * 12), 1 << 20, ctypes.byref(ws),
+                               None) == 0
+
+
+def test_align_validation(L):
+    fake = 1 << 20
+    n = ctypes.c_size_t(0)
+    A = L.moe_align
+    assert A(fake, 4, 2, 8, 24, fake, fake, fake, 1024, None, ctypes.byref(n), None) == -2
+    assert A(fake, 4, 9, 8, 16, fake, fake, fake, 1024, None, ctypes.byref(n), None) == -2
+    assert A(fake, -1, 2, 8, 16, fake, fake, fake, 1024, None, ctypes.byref(n), None) == -2
+    cap = L.moe_align_capacity(4, 2, 8, 16)
+    assert A(fake, 4, 2, 8, 16, fake, fake, fake, cap - 1, None, ctypes.byref(n), None) == -3
+    assert A(fake, 4, 2, 8, 16, None, fake, fake, cap, None, ctypes.byref(n), None) == -1
+    assert A(fake, 4, 2, 8, 16, fake + 1, fake, fake, cap, None, ctypes.byref(n), None) == -5
+    assert A(fake, 4, 2, 8, 16, fake, fake, fake, cap, None, None, None) == -1
+    # large inputs need a workspace: size query launches nothing
+    n = ctypes.c_size_t(0)
+    assert A(fake, 8192, 8, 128, 64, fake, fake, fake, 1 << 20, None, ctypes.byref(n), None) == 0
+    assert n.value > 0
+    small = ctypes.c_size_t(n.value - 1)
+    cap = L.moe_align_capacity(8192, 8, 128, 64)
+    assert A(fake, 8192, 8, 128, 64, fake, fake, fake, cap, fake, ctypes.byref(small), None) == -3
+
+
+def test_grouped_gemm_validation(L):
+    fake = 1 << 20
+    base = dict(a=fake, a_row_div=2, w=fake, E=8, N=64, K=64, sorted_token_ids=fake,
+                expert_ids=fake, num_tokens_post_padded=fake, block_m=16, num_valid=8,
+                capacity=128, epilogue=0, topk_weights=None, c=fake, c_is_fp32=1)
+
+    def call(**kw):
+        d = dict(base)
+        d.update(kw)
+        args = M.MoeGemmArgs(**d)
+        n = ctypes.c_size_t(7)
+        return L.moe_grouped_gemm(ctypes.byref(args), None, ctypes.byref(n), None)
+
+    assert call(K=60) == -2
+    assert call(N=60) == -2
+    assert call(epilogue=1, N=56) == -2
+    assert call(epilogue=4) == -2
+    assert call(block_m=48) == -2
+    assert call(capacity=100) == -2
+    assert call(E=0) == -2
+    assert call(num_valid=7) == -2         # not a multiple of a_row_div
+    assert call(a=None) == -1
+    assert call(epilogue=3) == -1          # weighted scatter needs weights
+    assert call(w=fake + 8) == -5
+    assert call(capacity=0) == 0           # nothing to do

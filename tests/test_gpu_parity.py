@@ -1,0 +1,207 @@
+"""GPU parity: libmoe's HIP path (through the C ABI) against the CPU oracle.
+
+Routing outputs are compared bit for bit; the fp32 layer output within
+max|d| <= 2e-2 and rel-L2 <= 5e-3; intermediate grouped-GEMM outputs within a
+bound derived from bf16 rounding of the result (2^-8 relative) plus fp32
+accumulation-order differences.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+
+from grouped_gemm_topk_amd import workloads as W
+from oracle import moe_oracle as O
+from tests.helpers import assert_out_close, to_dev
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def moe():
+    from grouped_gemm_topk_amd import moe as M
+    M.lib()
+    return M
+
+
+def _check_routing(res_gpu, ref, T, k, bm):
+    ids = res_gpu["topk_ids"].cpu().numpy()
+    assert np.array_equal(ids, ref["topk_ids"]), "topk_ids"
+    np.testing.assert_allclose(res_gpu["topk_weights"].cpu().numpy(), ref["topk_weights"],
+                               rtol=2e-6, atol=1e-7)
+    ntpp = int(res_gpu["num_tokens_post_padded"].cpu().item())
+    assert ntpp == ref["num_tokens_post_padded"]
+    st = res_gpu["sorted_token_ids"].cpu().numpy()[:ntpp]
+    assert np.array_equal(st, ref["sorted_token_ids"]), "sorted_token_ids"
+    ex = res_gpu["expert_ids"].cpu().numpy()[:ntpp // bm]
+    assert np.array_equal(ex, ref["expert_ids"]), "expert_ids"
+
+
+def _run_fused(moe, cfg, inp, block_m=None):
+    p = moe.LayerParams.from_config(cfg, block_m=block_m)
+    args = [to_dev(inp["x"]), to_dev(inp["logits"]), to_dev(inp["w13"]), to_dev(inp["w2"])]
+    sh = [to_dev(inp["shared_w13"]), to_dev(inp["shared_w2"])] if cfg.n_shared else [None, None]
+    out, routing = moe.moe_fused_forward(p, *args, *sh, return_routing=True)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), routing
+
+
+# ---------------------------------------------------------------- align
+@pytest.mark.parametrize("bm", [16, 32, 64, 128])
+@pytest.mark.parametrize("T,k,E,mode", [
+    (1, 8, 128, "rand"), (3, 8, 128, "rand"), (37, 2, 8, "rand"), (64, 2, 8, "rand"),
+    (100, 4, 18, "rand"), (513, 6, 128, "rand"), (700, 8, 256, "rand"),
+    (4096, 4, 18, "rand"), (8192, 8, 128, "zipf"), (5000, 1, 1, "rand"), (1023, 5, 64, "one"),
+    (0, 4, 8, "rand"), (2049, 2, 8, "rand"),
+])
+def test_align_bit_exact(moe, T, k, E, mode, bm):
+    print(f"align T={T} k={k} E={E} mode={mode} bm={bm}", flush=True)
+    rng = np.random.default_rng(T * 7 + E + bm)
+    if mode == "rand":
+        ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32) if T else \
+            np.zeros((0, k), np.int32)
+    elif mode == "one":      # every slot on expert 3
+        ids = np.full((T, k), 3, np.int32)
+    else:                     # skewed
+        pr = 1.0 / np.arange(1, E + 1) ** 1.1
+        ids = np.stack([rng.choice(E, size=k, replace=False, p=pr / pr.sum())
+                        for _ in range(T)]).astype(np.int32)
+    ref = O.align(ids, E, bm)
+    dev_ids = torch.from_numpy(ids).cuda() if T else torch.zeros((0, k), dtype=torch.int32,
+                                                                 device="cuda")
+    st, ex, ntpp = moe.moe_align(dev_ids, E, bm)
+    torch.cuda.synchronize()
+    n = int(ntpp.cpu().item())
+    assert n == ref["num_tokens_post_padded"]
+    assert np.array_equal(st.cpu().numpy()[:n], ref["sorted_token_ids"])
+    assert np.array_equal(ex.cpu().numpy()[:n // bm], ref["expert_ids"])
+
+
+# ---------------------------------------------------------------- grouped GEMM
+@pytest.mark.parametrize("bm", [16, 32, 64, 128])
+@pytest.mark.parametrize("epi,c32", [(O.EPI_STORE, 1), (O.EPI_STORE, 0), (O.EPI_SWIGLU, 0),
+                                     (O.EPI_RELU2, 0), (O.EPI_WEIGHTED_SCATTER, 1),
+                                     (O.EPI_SWIGLU, 1)])
+@pytest.mark.parametrize("shape", [(45, 3, 6, 200, 80), (300, 2, 5, 136, 272)])
+def test_grouped_gemm_vs_oracle(moe, shape, epi, c32, bm):
+    T, k, E, K, N = shape
+    print(f"grouped_gemm shape={shape} epi={epi} fp32={c32} bm={bm}", flush=True)
+    rng = np.random.default_rng(T + 31 * epi + bm)
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    wts = rng.random((T, k)).astype(np.float32)
+    x_bits = W.f32_to_bf16_bits(rng.standard_normal((T, K)).astype(np.float32))
+    w_bits = W.f32_to_bf16_bits((0.1 * rng.standard_normal((E, N, K))).astype(np.float32))
+    dev_ids = torch.from_numpy(ids).cuda()
+    st, ex, ntpp = moe.moe_align(dev_ids, E, bm)
+    al = O.align(ids, E, bm)
+    ref = O.grouped_gemm(O.bf16_to_f64(x_bits), k, O.bf16_to_f64(w_bits), al["sorted_token_ids"],
+                         al["expert_ids"], al["num_tokens_post_padded"], bm, T * k, epi, wts)
+    cap = st.numel()
+    ncols = N // 2 if epi == O.EPI_SWIGLU else N
+    rows = T * k if epi == O.EPI_WEIGHTED_SCATTER else cap
+    dt = torch.float32 if c32 else torch.bfloat16
+    c = torch.full((rows, ncols), float("nan"), dtype=dt, device="cuda")
+    moe.moe_grouped_gemm(to_dev(x_bits), k, to_dev(w_bits), st, ex, ntpp, bm, T * k, epi, c,
+                         torch.from_numpy(wts.reshape(-1)).cuda())
+    torch.cuda.synchronize()
+    got = c.float().cpu().numpy()
+    nt = al["num_tokens_post_padded"]
+    if epi != O.EPI_WEIGHTED_SCATTER:
+        got, ref = got[:nt], ref[:nt]
+    assert np.all(np.isfinite(got)), "rows left unwritten"
+    tol = (2.0 ** -8 if not c32 else 1e-5) * np.abs(ref) + 1e-4 * np.abs(ref).max()
+    bad = np.abs(got - ref) > tol
+    assert not bad.any(), f"{bad.sum()} mismatches, worst {np.abs(got - ref).max()}"
+
+
+def test_grouped_gemm_contiguous_a(moe):
+    """a_row_div = 0: A is read in padded order (the second GEMM's form)."""
+    T, k, E, K, N, bm = 50, 2, 4, 96, 64, 32
+    rng = np.random.default_rng(77)
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    wts = rng.random((T, k)).astype(np.float32)
+    st, ex, ntpp = moe.moe_align(torch.from_numpy(ids).cuda(), E, bm)
+    al = O.align(ids, E, bm)
+    cap = st.numel()
+    a_bits = W.f32_to_bf16_bits(rng.standard_normal((cap, K)).astype(np.float32))
+    w_bits = W.f32_to_bf16_bits((0.1 * rng.standard_normal((E, N, K))).astype(np.float32))
+    ref = O.grouped_gemm(O.bf16_to_f64(a_bits), 0, O.bf16_to_f64(w_bits), al["sorted_token_ids"],
+                         al["expert_ids"], al["num_tokens_post_padded"], bm, T * k,
+                         O.EPI_WEIGHTED_SCATTER, wts)
+    c = torch.full((T * k, N), float("nan"), dtype=torch.float32, device="cuda")
+    moe.moe_grouped_gemm(to_dev(a_bits), 0, to_dev(w_bits), st, ex, ntpp, bm, T * k,
+                         O.EPI_WEIGHTED_SCATTER, c, torch.from_numpy(wts.reshape(-1)).cuda())
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(c.cpu().numpy(), ref, rtol=1e-5, atol=1e-4)
+
+
+# ---------------------------------------------------------------- fused forward, small
+SMALL = [
+    W.CONFIGS["tiny"],
+    W.small_config("small_swiglu", T=37, H=64, I=96, E=8, top_k=2),
+    W.small_config("small_relu2", T=50, H=136, I=72, E=16, top_k=3, activation=W.ACT_RELU2),
+    W.small_config("small_dsv3", T=70, H=128, I=64, E=18, top_k=4, scoring=W.SCORE_SIGMOID,
+                   n_group=6, topk_group=4, n_shared=1, block_m=32),
+    W.small_config("small_dsv3_s2.5", T=70, H=128, I=64, E=18, top_k=4, scoring=W.SCORE_SIGMOID,
+                   n_group=6, topk_group=4, n_shared=1, scale=2.5, block_m=64),
+    W.small_config("small_e128", T=9, H=256, I=128, E=128, top_k=8),
+    W.small_config("small_norenorm", T=40, H=64, I=64, E=32, top_k=4, renormalize=0),
+    W.small_config("small_sigmoid_flat", T=33, H=64, I=32, E=12, top_k=3,
+                   scoring=W.SCORE_SIGMOID, renormalize=0),
+    W.small_config("small_one_token", T=1, H=96, I=40, E=8, top_k=8),
+    W.small_config("small_many_tokens", T=300, H=64, I=48, E=8, top_k=2, block_m=128),
+    W.small_config("small_k1", T=65, H=64, I=64, E=4, top_k=1, block_m=64),
+]
+
+
+@pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
+@pytest.mark.parametrize("bm", [None, 16, 128])
+def test_fused_forward_small(moe, cfg, bm):
+    print(f"fused {cfg.name} bm={bm}", flush=True)
+    inp = W.make_inputs(cfg)
+    ref = O.moe_forward_cfg(cfg if bm is None else dataclasses.replace(cfg, block_m=bm), inp)
+    out, routing = _run_fused(moe, cfg, inp, bm)
+    _check_routing(routing, ref, cfg.T, cfg.top_k, bm or cfg.block_m)
+    assert_out_close(out, ref["out"], cfg.name)
+
+
+def test_fused_forward_zero_tokens(moe):
+    cfg = W.small_config("t0", T=0, H=64, I=32, E=8, top_k=2)
+    p = moe.LayerParams.from_config(cfg)
+    z = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    out = moe.moe_fused_forward(p, z, torch.empty((0, 8), device="cuda"),
+                                torch.zeros((8, 64, 64), dtype=torch.bfloat16, device="cuda"),
+                                torch.zeros((8, 64, 32), dtype=torch.bfloat16, device="cuda"))
+    assert out.shape == (0, 64)
+
+
+# ---------------------------------------------------------------- full-size configs
+def _full_case(moe, name, n_sample=None):
+    cfg = W.CONFIGS[name]
+    print(f"full-size {name}", flush=True)
+    inp = W.make_inputs(cfg)
+    # routing at full size from the oracle (cheap); the output on sampled tokens
+    ids, wts = O.gate(inp["logits"], cfg.top_k, cfg.scoring, cfg.n_group, cfg.topk_group,
+                      cfg.renormalize, cfg.scale)
+    ref = {"topk_ids": ids, "topk_weights": wts, **O.align(ids, cfg.E, cfg.block_m)}
+    out, routing = _run_fused(moe, cfg, inp)
+    _check_routing(routing, ref, cfg.T, cfg.top_k, cfg.block_m)
+    rng = np.random.default_rng(5)
+    toks = np.arange(cfg.T) if n_sample is None or n_sample >= cfg.T else \
+        np.unique(np.concatenate([[0, cfg.T - 1], rng.choice(cfg.T, n_sample, replace=False)]))
+    want = np.stack([O.token_output(inp, int(t), ids[t], wts[t], cfg.activation, cfg.n_shared)
+                     for t in toks])
+    return assert_out_close(out[toks], want, name)
+
+
+@pytest.mark.parametrize("name", ["decode_t1", "decode_t3", "decode_t8", "relu2_t1", "relu2_t16"])
+def test_full_decode_configs(moe, name):
+    _full_case(moe, name)
+
+
+@pytest.mark.parametrize("name,n", [("dsv3", 48), ("dsv3_s2.5", 48), ("zipf128", 48),
+                                    ("relu2_t2048", 48)])
+def test_full_prefill_configs_sampled(moe, name, n):
+    _full_case(moe, name, n)
