@@ -1,0 +1,247 @@
+"""Benchmark of the fused MoE forward (libmoe) on one MI355X.
+
+One step = one moe_fused_forward call over one batch (gating, align, GEMM1 +
+activation, GEMM2 + routed weight, combine) on the DeepSeek-V3-8B-shaped layer
+(T=4096, H=3072, I=2560, 18 routed experts top-4 with grouped sigmoid routing,
+one shared expert, SwiGLU, bf16 weights).  Inputs are seeded synthetic tensors
+resident in HBM before timing starts.
+
+Prints ONE JSON line: TFLOPS of the layer (2*T*k_eff*3*H*I / latency), the
+roofline entry of the dominant kernel (the SwiGLU grouped GEMM, timed alone
+with HIP events on its stream), decode microseconds per layer at T = 1, 3, 8
+(128 experts top-8, cycling through enough distinct layers that the 256 MB
+Infinity Cache cannot hold the touched weights), and the CPU oracle's rate on
+a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+MALL_BYTES = 256 << 20           # Infinity Cache
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="dsv3")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode measurements")
+    ap.add_argument("--cpu-tokens", type=int, default=2048,
+                    help="tokens of the workload the CPU oracle runs on")
+    ap.add_argument("--extra", default="", help="comma list of more configs to time (report only)")
+    return ap.parse_args()
+
+
+def _to_dev(a, torch):
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _layer(cfg, inp, torch, moe, routing=False, weights=None):
+    p = moe.LayerParams.from_config(cfg)
+    w = weights or {k: _to_dev(inp[k], torch) for k in ("w13", "w2", "shared_w13", "shared_w2")
+                    if k in inp}
+    return moe.FusedLayer(p, _to_dev(inp["x"], torch), _to_dev(inp["logits"], torch), w["w13"],
+                          w["w2"], w.get("shared_w13"), w.get("shared_w2"),
+                          routing_outputs=routing), w
+
+
+def time_layer(layer, steps, warmup, torch):
+    for _ in range(warmup):
+        layer.run()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(s)
+    for _ in range(steps):
+        layer.run()
+    e1.record(s)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return e0.elapsed_time(e1) / steps, wall
+
+
+def time_dominant_gemm(cfg, layer, steps, warmup, torch, moe):
+    """The SwiGLU grouped GEMM (GEMM1 of the routed experts) alone, same inputs
+    and launch configuration as inside the layer, timed with events on the
+    stream it is launched on."""
+    r = layer.routing
+    t = layer.tensors
+    cap = r["sorted_token_ids"].numel()
+    act = torch.empty((cap, cfg.I), dtype=torch.bfloat16, device="cuda")
+
+    def go():
+        moe.moe_grouped_gemm(t["x"], cfg.top_k, t["w13"], r["sorted_token_ids"], r["expert_ids"],
+                             r["num_tokens_post_padded"], cfg.block_m, cfg.T * cfg.top_k,
+                             moe.EPI_SWIGLU, act)
+    for _ in range(warmup):
+        go()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(steps):
+        go()
+    e1.record(s)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def decode_case(name, torch, moe, W, O, reps=20):
+    """µs per layer at decode shape, cycling L distinct copies of the weights."""
+    cfg = W.CONFIGS[name]
+    inp = W.make_inputs(cfg)
+    ids, _ = O.gate(inp["logits"], cfg.top_k, cfg.scoring, cfg.n_group, cfg.topk_group,
+                    cfg.renormalize, cfg.scale)
+    touched = int(np.unique(ids).size)
+    per_expert = cfg.mats * cfg.H * cfg.I * 2
+    wbytes = touched * per_expert
+    nlayers = max(2, int(np.ceil(4 * MALL_BYTES / wbytes)))
+    base = {k: _to_dev(inp[k], torch) for k in ("w13", "w2")}
+    layers = []
+    for li in range(nlayers):
+        w = base if li == 0 else {k: v.clone() for k, v in base.items()}
+        layers.append(_layer(cfg, inp, torch, moe, weights=w)[0])
+    for l in layers:
+        l.run()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for l in layers:
+            l.run()
+    torch.cuda.synchronize()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (reps * nlayers)
+    alg_bytes = wbytes + cfg.T * cfg.H * 2 + cfg.T * cfg.H * 4 + cfg.T * cfg.E * 4
+    gbs = alg_bytes / (us * 1e-6) / 1e9
+    # parity of the last layer's output against the oracle (all tokens)
+    out = layers[0].run().cpu().numpy()
+    torch.cuda.synchronize()
+    ref = O.moe_forward_cfg(cfg, inp)["out"]
+    err = float(np.abs(out - ref).max())
+    del layers, base
+    torch.cuda.empty_cache()
+    return {"T": cfg.T, "us_per_layer": round(us, 2), "touched_experts": touched,
+            "alg_bytes": int(alg_bytes), "GBps": round(gbs, 1),
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "layers_cycled": nlayers,
+            "max_abs_err": err}
+
+
+def cpu_baseline(cfg, inp, ntok, W, O):
+    """The CPU oracle as it stands on the first ``ntok`` tokens of the workload."""
+    sub = {k: v for k, v in inp.items()}
+    sub["x"] = inp["x"][:ntok]
+    sub["logits"] = inp["logits"][:ntok]
+    threads = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas = threads
+    t0 = time.perf_counter()
+    O.moe_forward_cfg(cfg, sub)
+    dt = time.perf_counter() - t0
+    flops = cfg.flops() * ntok / cfg.T
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOPS", "cores": int(min(threads, blas)),
+            "kind": "oracle",
+            "sample": f"first {ntok} of {cfg.T} tokens of the {cfg.name} layer "
+                      f"({dt:.2f} s, fp64 numpy per-expert loop incl. weight widening)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this "
+              f"build (the MoE layer runs on a single MI355X).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from grouped_gemm_topk_amd import moe
+    from grouped_gemm_topk_amd import workloads as W
+    from oracle import moe_oracle as O
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    moe.lib()
+    cfg = W.CONFIGS[args.config]
+    inp = W.make_inputs(cfg)
+    layer, _ = _layer(cfg, inp, torch, moe, routing=True)
+    layer.run()
+    torch.cuda.synchronize()
+    print(f"# {cfg.name}: inputs resident, timing {args.steps} steps", file=sys.stderr, flush=True)
+    ms, wall = time_layer(layer, args.steps, args.warmup, torch)
+    flops = cfg.flops()
+    tflops = flops / (ms * 1e-3) / 1e12
+    # dominant kernel: routed SwiGLU grouped GEMM
+    gemm_ms = time_dominant_gemm(cfg, layer, args.steps, args.warmup, torch, moe)
+    gemm_flops = 2.0 * cfg.T * cfg.top_k * cfg.H * 2 * cfg.I
+    gemm_tf = gemm_flops / (gemm_ms * 1e-3) / 1e12
+    line = {
+        "metric": "fused-MoE layer TFLOPS at T=4096 + decode us/layer (T=1..8) vs roofline",
+        "value": round(tflops, 2), "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} "
+                               f"top_k={cfg.top_k} groups={cfg.n_group}/{cfg.topk_group} "
+                               f"shared={cfg.n_shared} block_m={cfg.block_m} SwiGLU bf16",
+                   "T": cfg.T, "H": cfg.H, "I": cfg.I, "E": cfg.E, "top_k": cfg.top_k,
+                   "block_m": cfg.block_m, "flops_per_step": flops,
+                   "routed_only_TFLOPS": round(cfg.flops(routed_only=True) / (ms * 1e-3) / 1e12, 2),
+                   "mfma_frac_of_layer": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                   "wall_s_timed": round(wall, 3)},
+        "roofline": {"bound": "mfma", "kernel": "grouped_gemm_kernel<128,256,2,2,SwiGLU>",
+                     "achieved": round(gemm_tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(gemm_tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "avg_launch_us": round(gemm_ms * 1e3, 2),
+                     "alg_flops_per_launch": gemm_flops},
+    }
+    if not args.no_decode:
+        line["decode"] = [decode_case(n, torch, moe, W, O) for n in
+                          ("decode_t1", "decode_t3", "decode_t8")]
+    extra = [e for e in args.extra.split(",") if e]
+    if extra:
+        line["extra"] = {}
+        for name in extra:
+            c2 = W.CONFIGS[name]
+            i2 = W.make_inputs(c2)
+            l2, _ = _layer(c2, i2, torch, moe)
+            ms2, _ = time_layer(l2, args.steps, args.warmup, torch)
+            line["extra"][name] = {"ms": round(ms2, 4),
+                                   "TFLOPS": round(c2.flops() / (ms2 * 1e-3) / 1e12, 2)}
+            del l2
+            torch.cuda.empty_cache()
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(cfg, inp, min(args.cpu_tokens, cfg.T), W, O)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

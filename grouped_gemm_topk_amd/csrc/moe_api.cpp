@@ -161,15 +161,14 @@ int moe_align(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E, int32_t 
   const int64_t n = (int64_t)T * k;
   if (n > (1 << 28)) return MOE_ERR_SHAPE;
   const size_t need = align_scratch_bytes(n, E);
-  if (!workspace && need > 0) {
+  if (!workspace) {
     *workspace_bytes = need;
     return MOE_OK;
   }
-  if (!workspace) *workspace_bytes = 0;
-  if (!sorted_token_ids || !expert_ids || !num_tokens_post_padded) return MOE_ERR_NULL;
-  if (n > 0 && !topk_ids) return MOE_ERR_NULL;
+  if (!num_tokens_post_padded) return MOE_ERR_NULL;
+  if (n > 0 && (!topk_ids || !sorted_token_ids || !expert_ids)) return MOE_ERR_NULL;
   if (capacity < MOE_ALIGN_CAPACITY(T, k, E, block_m)) return MOE_ERR_CAPACITY;
-  if (workspace && *workspace_bytes < need) return MOE_ERR_CAPACITY;
+  if (*workspace_bytes < need) return MOE_ERR_CAPACITY;
   if (!aligned4(topk_ids) || !aligned4(sorted_token_ids) || !aligned4(expert_ids) ||
       !aligned4(num_tokens_post_padded) || !aligned16(workspace))
     return MOE_ERR_ALIGN;
@@ -183,7 +182,7 @@ int moe_align(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E, int32_t 
 int moe_grouped_gemm(const moe_gemm_args* args, void* workspace, size_t* workspace_bytes,
                      void* stream) {
   (void)workspace;
-  if (!args || !workspace_bytes) return MOE_ERR_NULL;
+  if (!args) return MOE_ERR_NULL;
   const moe_gemm_args& g = *args;
   if (g.E < 1 || g.E > MOE_MAX_EXPERTS || g.N <= 0 || g.K <= 0) return MOE_ERR_SHAPE;
   if (g.K % 8 != 0 || g.N % 8 != 0) return MOE_ERR_SHAPE;
@@ -194,7 +193,7 @@ int moe_grouped_gemm(const moe_gemm_args* args, void* workspace, size_t* workspa
   if (g.num_valid < 0 || g.a_row_div < 0) return MOE_ERR_SHAPE;
   if (g.a_row_div > 0 && g.num_valid % g.a_row_div != 0) return MOE_ERR_SHAPE;
   if (g.c_is_fp32 != 0 && g.c_is_fp32 != 1) return MOE_ERR_SHAPE;
-  *workspace_bytes = 0;   // this call needs no workspace and always runs
+  if (workspace_bytes) *workspace_bytes = 0;   // this call needs no workspace
   if (g.capacity == 0) return MOE_OK;
   if (!g.a || !g.w || !g.c || !g.sorted_token_ids || !g.expert_ids || !g.num_tokens_post_padded)
     return MOE_ERR_NULL;

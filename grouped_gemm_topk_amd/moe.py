@@ -136,10 +136,8 @@ def moe_align(topk_ids: torch.Tensor, E: int, block_m: int, sorted_token_ids=Non
     if workspace is None:
         _check("moe_align", L.moe_align(_ptr(topk_ids), T, k, E, block_m, None, None, None, cap,
                                         None, ctypes.byref(n), None))
-        if n.value > 0:
-            workspace = _workspace(n.value, dev)
-    if workspace is not None:
-        n = ctypes.c_size_t(workspace.numel())
+        workspace = _workspace(n.value, dev)
+    n = ctypes.c_size_t(workspace.numel())
     _check("moe_align", L.moe_align(_ptr(topk_ids), T, k, E, block_m, _ptr(sorted_token_ids),
                                     _ptr(expert_ids), _ptr(num_tokens_post_padded),
                                     sorted_token_ids.numel(), _ptr(workspace), ctypes.byref(n),

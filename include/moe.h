@@ -19,11 +19,12 @@
  * - The caller owns every buffer, including the workspace.  The library never
  *   allocates device memory, never synchronises the stream and never copies to
  *   the host.  All work is enqueued asynchronously on `stream`.
- * - Workspace: `workspace_bytes` must not be NULL.  When a call needs a
- *   workspace and `workspace == NULL`, the required byte count is written to
- *   `*workspace_bytes` and nothing is launched; call again with a buffer of at
- *   least that many bytes and its size in `*workspace_bytes`.  A call that
- *   needs none (required size 0) writes 0 to `*workspace_bytes` and runs.
+ * - Workspace (moe_align, moe_fused_forward): `workspace_bytes` must not be
+ *   NULL.  With `workspace == NULL` the call only writes the required byte
+ *   count (possibly 0) to `*workspace_bytes` and launches nothing; call again
+ *   with a non-NULL buffer of at least that many bytes and its size in
+ *   `*workspace_bytes`.  moe_grouped_gemm needs no workspace and ignores both
+ *   arguments.
  * - Arguments are validated on the host before anything is launched; a
  *   negative status is returned and nothing is written.  There is no fallback
  *   path: an unsupported case is an error.  HIP failures are returned as

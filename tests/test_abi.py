@@ -104,24 +104,36 @@ def test_fused_forward_t0_is_noop(L):
 
 
 def test_align_validation(L):
-    fake = 1 << 20
-    n = ctypes.c_size_t(0)
+    fake = 1 << 20           # never dereferenced: validation fails first
     A = L.moe_align
-    assert A(fake, 4, 2, 8, 24, fake, fake, fake, 1024, None, ctypes.byref(n), None) == -2
-    assert A(fake, 4, 9, 8, 16, fake, fake, fake, 1024, None, ctypes.byref(n), None) == -2
-    assert A(fake, -1, 2, 8, 16, fake, fake, fake, 1024, None, ctypes.byref(n), None) == -2
-    cap = L.moe_align_capacity(4, 2, 8, 16)
-    assert A(fake, 4, 2, 8, 16, fake, fake, fake, cap - 1, None, ctypes.byref(n), None) == -3
-    assert A(fake, 4, 2, 8, 16, None, fake, fake, cap, None, ctypes.byref(n), None) == -1
-    assert A(fake, 4, 2, 8, 16, fake + 1, fake, fake, cap, None, ctypes.byref(n), None) == -5
-    assert A(fake, 4, 2, 8, 16, fake, fake, fake, cap, None, None, None) == -1
-    # large inputs need a workspace: size query launches nothing
+
+    def call(ids=fake, T=4, k=2, E=8, bm=16, st=fake, ex=fake, nt=fake, cap=None, ws=fake,
+             wsb=1 << 30):
+        if cap is None:
+            cap = max(L.moe_align_capacity(T, k, E, bm), 0)
+        n = ctypes.c_size_t(wsb or 0)
+        return A(ids, T, k, E, bm, st, ex, nt, cap, ws, None if wsb is None else ctypes.byref(n),
+                 None)
+
+    assert call(bm=24) == -2
+    assert call(k=9) == -2
+    assert call(T=-1) == -2
+    assert call(k=17, E=32) == -2
+    assert call(E=300, k=2) == -2
+    assert call(cap=L.moe_align_capacity(4, 2, 8, 16) - 1) == -3
+    assert call(st=None) == -1
+    assert call(ids=None) == -1
+    assert call(st=fake + 1) == -5
+    assert call(ws=fake + 4) == -5
+    assert call(wsb=None) == -1
+    # a NULL workspace is a size query: nothing else is checked or launched
+    n = ctypes.c_size_t(5)
+    assert A(None, 4, 2, 8, 16, None, None, None, 0, None, ctypes.byref(n), None) == 0
+    assert n.value == 0
     n = ctypes.c_size_t(0)
     assert A(fake, 8192, 8, 128, 64, fake, fake, fake, 1 << 20, None, ctypes.byref(n), None) == 0
     assert n.value > 0
-    small = ctypes.c_size_t(n.value - 1)
-    cap = L.moe_align_capacity(8192, 8, 128, 64)
-    assert A(fake, 8192, 8, 128, 64, fake, fake, fake, cap, fake, ctypes.byref(small), None) == -3
+    assert call(T=8192, k=8, E=128, bm=64, wsb=n.value - 1) == -3
 
 
 def test_grouped_gemm_validation(L):
