@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--config", default="dsv3")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode measurements")
-    ap.add_argument("--cpu-tokens", type=int, default=2048,
+    ap.add_argument("--cpu-tokens", type=int, default=4096,
                     help="tokens of the workload the CPU oracle runs on")
     ap.add_argument("--extra", default="", help="comma list of more configs to time (report only)")
     return ap.parse_args()
@@ -154,8 +154,9 @@ def decode_case(name, torch, moe, W, O, reps=20):
             "max_abs_err": err}
 
 
-def cpu_baseline(cfg, inp, ntok, W, O):
-    """The CPU oracle as it stands on the first ``ntok`` tokens of the workload."""
+def cpu_baseline(cfg, inp, ntok, W, O, min_seconds=10.0):
+    """The CPU oracle as it stands on the first ``ntok`` tokens of the workload,
+    repeated until at least ``min_seconds`` of CPU work have been timed."""
     sub = {k: v for k, v in inp.items()}
     sub["x"] = inp["x"][:ntok]
     sub["logits"] = inp["logits"][:ntok]
@@ -165,21 +166,26 @@ def cpu_baseline(cfg, inp, ntok, W, O):
         blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         blas = threads
+    reps = 0
     t0 = time.perf_counter()
-    O.moe_forward_cfg(cfg, sub)
-    dt = time.perf_counter() - t0
-    flops = cfg.flops() * ntok / cfg.T
+    while True:
+        O.moe_forward_cfg(cfg, sub)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds or reps >= 50:
+            break
+    flops = cfg.flops() * ntok / cfg.T * reps
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOPS", "cores": int(min(threads, blas)),
             "kind": "oracle",
-            "sample": f"first {ntok} of {cfg.T} tokens of the {cfg.name} layer "
+            "sample": f"{reps} x the first {ntok} of {cfg.T} tokens of the {cfg.name} layer "
                       f"({dt:.2f} s, fp64 numpy per-expert loop incl. weight widening)"}
 
 
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this "
-              f"build (the MoE layer runs on a single MI355X).", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              f"(the MoE layer runs on a single MI355X).", file=sys.stderr)
         sys.exit(2)
     import torch
 
