@@ -286,6 +286,31 @@ int moe_fused_forward(const moe_layer_params* p, const void* x, const float* rou
   }
   if (e != hipSuccess) return hip_status(e);
 
+  // ---- decode shapes: expert GEMVs, each touched expert's weights read once
+  if (T <= moe::kGemvMaxTokens) {
+    moe::GemvParams gv{};
+    gv.x = (const uint16_t*)x;
+    gv.w13 = (const uint16_t*)w13;
+    gv.w2 = (const uint16_t*)w2;
+    gv.sw13 = p->n_shared ? (const uint16_t*)shared_w13 : nullptr;
+    gv.sw2 = p->n_shared ? (const uint16_t*)shared_w2 : nullptr;
+    gv.sorted_ids = sorted;
+    gv.expert_ids = eids;
+    gv.ntpp = ntpp;
+    gv.topk_w = wts;
+    gv.T = T;
+    gv.H = H;
+    gv.I = I;
+    gv.k = k;
+    gv.E = E;
+    gv.bm = bm;
+    gv.nblk = (int)(n < E ? n : E);
+    gv.act = L.act;
+    gv.act_sh = L.act_sh;
+    gv.out = out;
+    return hip_status(moe::launch_gemv(gv, p->activation == MOE_ACT_SWIGLU, s));
+  }
+
   // ---- GEMM1 + activation: act[i] = act(x[sorted[i] / k] . w13[e]^T)
   const int epi1 = p->activation == MOE_ACT_SWIGLU ? MOE_EPI_SWIGLU : MOE_EPI_RELU2;
   moe::GemmParams g1{};

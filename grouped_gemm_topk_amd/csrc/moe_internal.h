@@ -58,6 +58,28 @@ struct GemmParams {
   int ldc;                  // output row stride in elements
 };
 
+// ---------------------------------------------------------------- decode GEMVs
+constexpr int kGemvMaxTokens = 16;     // T at or below this takes the GEMV path
+
+struct GemvParams {
+  const uint16_t* x;        // [T, H]
+  const uint16_t* w13;      // [E, M1, H]
+  const uint16_t* w2;       // [E, H, I]
+  const uint16_t* sw13;     // shared expert [M1, H] or null
+  const uint16_t* sw2;      // shared expert [H, I] or null
+  const int* sorted_ids;
+  const int* expert_ids;
+  const int* ntpp;
+  const float* topk_w;      // [T * k]
+  int T, H, I, k, E, bm;
+  int nblk;                 // routed blocks that can exist: min(E, T * k)
+  uint16_t* act;            // [capacity, I] rows in padded order
+  uint16_t* act_sh;         // [T, I]
+  float* out;               // [T, H], zeroed by GEMV1, accumulated by GEMV2
+};
+
+hipError_t launch_gemv(const GemvParams& p, bool swiglu, hipStream_t s);
+
 hipError_t launch_gate(const GateParams& p, hipStream_t s);
 hipError_t launch_route_fused(const GateParams& g, const AlignParams& a, hipStream_t s);
 hipError_t launch_align(const AlignParams& p, hipStream_t s);

@@ -153,6 +153,12 @@ SMALL = [
     W.small_config("small_one_token", T=1, H=96, I=40, E=8, top_k=8),
     W.small_config("small_many_tokens", T=300, H=64, I=48, E=8, top_k=2, block_m=128),
     W.small_config("small_k1", T=65, H=64, I=64, E=4, top_k=1, block_m=64),
+    # decode shapes (T <= 16 takes the GEMV path)
+    W.small_config("small_dsv3_decode", T=5, H=136, I=72, E=18, top_k=4, scoring=W.SCORE_SIGMOID,
+                   n_group=6, topk_group=4, n_shared=1, block_m=128),
+    W.small_config("small_relu2_t16", T=16, H=264, I=40, E=32, top_k=6, activation=W.ACT_RELU2),
+    W.small_config("small_t17_gemm", T=17, H=64, I=48, E=8, top_k=2),
+    W.small_config("small_decode_ragged_k", T=3, H=600, I=328, E=64, top_k=8),
 ]
 
 
