@@ -1,24 +1,31 @@
-// Decode path (T <= 16 tokens): expert GEMVs that stream every touched
-// expert's weights from HBM once and apply them to all tokens routed to it.
+// Decode path (T <= 16 tokens): routing plus two expert GEMVs in two launches.
 //
-// The aligned layout already groups the slots of one expert into one block
-// (each expert has at most T <= 16 slots), which is the dedupe of duplicate
-// experts across tokens of the B70 grouped multi-token experiment (*Intent*):
-// one read of the expert's rows serves every token that picked it.  The
-// activation is fused into the first GEMV (SwiGLU of the axolotl DeepSeek-V3
-// MoE forward, relu^2 of the mlxcel fc1 kernel) and the routed weight plus the
-// sum over the k slots into the second (skill card *Common Pitfalls* 4).
+// The aligned layout groups the slots of one expert into one block (each
+// expert has at most T <= 16 slots), which is the dedupe of duplicate experts
+// across tokens of the B70 grouped multi-token experiment (*Intent*): one
+// read of an expert's rows serves every token that picked it.  The activation
+// is fused into the first GEMV (SwiGLU of the axolotl DeepSeek-V3 MoE forward,
+// relu^2 of the mlxcel fc1 kernel) and the routed weight plus the sum over the
+// k slots into the second (skill card *Common Pitfalls* 4).  That B70
+// experiment lost to a per-slot path because its grouping added scans,
+// scatters and register pressure; here the grouping costs nothing extra
+// because the routing itself produces it.
 //
-// gfx950 mapping.  The work is HBM-bound, so the kernels are shaped for bytes
-// in flight, not for MFMA rate: one v_mfma_f32_16x16x32_bf16 tile covers 16
-// weight rows x up to 16 tokens.  K is permuted inside each 256-wide round so
-// that every lane reads 128 contiguous bytes of one weight row (8 x 16-byte
-// loads) and the token operand is read with the same permutation; a sum over
-// k is indifferent to the order of its terms.  GEMV1 splits K across the 4
-// waves of a workgroup and reduces in LDS before the activation; GEMV2 gives
-// each wave its own 16 output rows and adds the weighted results into `out`
-// with fp32 atomics (the k slots of a token land in any order).
+// gfx950 mapping.  At decode the layer is HBM-bound and latency-bound:
+// * Routing (top-k gating and align for at most 256 slots) runs as a prologue
+//   of EVERY workgroup of GEMV1 from the router logits in LDS, so no separate
+//   routing launch sits on the critical path; workgroup (0,0) also writes the
+//   routing outputs that GEMV2 and the caller read.  Top-k uses ranks: each
+//   lane counts the experts that beat its own (logit, then lower index) with
+//   broadcast LDS reads, so there is no chain of cross-lane reductions.
+// * Weights are read once with coalesced nontemporal loads and staged through
+//   LDS into the operand layout of v_mfma_f32_16x16x32_bf16, whose tile covers
+//   16 weight rows x up to 16 tokens.  K is split across the waves of a
+//   workgroup and reduced in LDS.
+// * GEMV2 adds weight * result into `out` with fp32 atomics (the k slots of a
+//   token arrive in any order); GEMV1 zeroes `out` first.
 #include <hip/hip_runtime.h>
+#include <limits.h>
 
 #include "moe_internal.h"
 
@@ -30,7 +37,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kRound = 256;   // K elements per round: 4 lane groups x 64
+constexpr int kRound = 256;       // K elements per round: 8 MFMAs x 32
+constexpr int kMaxSlots = kGemvMaxTokens * 16;
 
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   unsigned u = __float_as_uint(f);
@@ -46,184 +54,482 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// Token rows of block b: for column j < 16 returns the token (or -1) and slot.
-struct BlockRows {
-  bool shared;
-  int base;      // first padded position of the block
-};
-
-__device__ __forceinline__ int block_token(const GemvParams& p, const BlockRows& br, int j,
-                                           int* slot) {
-  if (br.shared) {
-    *slot = -1;
-    return j < p.T ? j : -1;
-  }
-  int sid = p.sorted_ids[br.base + j];
-  if (sid < 0 || sid >= p.T * p.k) return -1;
-  *slot = sid;
-  return sid / p.k;
+__device__ __forceinline__ void wave_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
-// One 256-wide K round of a 16-row weight tile against 16 token rows.
-// w: this lane's weight row (null = zero row), b: this lane's token row (null =
-// zero), k0 = round start + 64 * lane group.
-__device__ __forceinline__ f32x4 round16(const uint16_t* w, const uint16_t* b, int k0, int K,
-                                         f32x4 acc) {
-  u32x4 wa[8], xb[8];
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// ------------------------------------------------------------------ routing prologue
+constexpr int kRow = kMaxExperts;   // LDS row of one token's logits, padded with -inf
+
+// 64-bit key whose unsigned order is (logit descending-equal ..., lower index
+// first): high word = order-preserving image of the float (-0 folded into +0,
+// so the two compare equal as floats do), low word = inverted expert index.
+__device__ __forceinline__ uint64_t order_key(float f, int e) {
+  unsigned u = __float_as_uint(f + 0.0f);
+  u ^= (unsigned)((int)u >> 31) | 0x80000000u;
+  return ((uint64_t)u << 32) | (uint64_t)(0xffffffffu - (unsigned)e);
+}
+
+// rank[i] += number of keys in row[0, n) above kown[i], for the NV own values.
+template <int NV>
+__device__ __forceinline__ void rank_keys(const uint64_t* row, int n, const uint64_t* kown,
+                                          int* rank) {
+  for (int e0 = 0; e0 < n; e0 += 16) {
+    uint64_t c[16];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const ulonglong2 two = *(const ulonglong2*)(row + e0 + 2 * q);
+      c[2 * q] = two.x;
+      c[2 * q + 1] = two.y;
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+#pragma unroll
+      for (int i = 0; i < NV; ++i) rank[i] += c[u] > kown[i] ? 1 : 0;
+  }
+}
+
+constexpr int kPrologueWaves = 4;
+
+struct RouteLds {
+  float wlog[kPrologueWaves][kRow];     // per-wave copy of one token's logits
+  uint64_t key[kPrologueWaves][kRow];   // per-wave order keys of one token
+  double gscore[kPrologueWaves][64];
+  double ex[kMaxSlots];        // per-slot exp / sigmoid terms of the weights
+  int ids[kMaxSlots];
+  float val[kMaxSlots];
+  float wts[kMaxSlots];
+  unsigned tokmask[kMaxExperts];  // bit t: token t picked the expert
+  int off[kMaxExperts];
+  int blk_expert[kMaxSlots];   // expert of each block (<= min(E, n) blocks)
+  int rowslot[16];             // slot of each of this workgroup's 16 rows (-1: none)
+  int ntpp;
+  int my_expert;               // expert of this workgroup's block, -1 if none
+};
+
+// Gating + align for all T <= 16 tokens by one workgroup of kPrologueWaves
+// waves.  Fills `L` and, when `write_out`, the routing outputs in global
+// memory.  `blk` is the block whose rows this workgroup needs (or -1).
+__device__ void route_prologue(const GemvParams& p, RouteLds& L, int blk, bool write_out) {
+  const int tid = threadIdx.x;
+  const int nthr = blockDim.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int T = p.T, E = p.E, k = p.k;
+  const int n = T * k;
+  const int Epad = (E + 15) & ~15;
+
+  for (int e = tid; e < E; e += nthr) L.tokmask[e] = 0u;
+  if (tid < 16) L.rowslot[tid] = -1;
+  __syncthreads();
+
+  // ---- gating: one wave per token
+  float* wl = L.wlog[wave];
+  uint64_t* wk = L.key[wave];
+  for (int t = wave; t < T; t += kPrologueWaves) {
+    float v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int e = lane + 64 * i;
+      v[i] = e < E ? p.logits[t * E + e] : -INFINITY;
+    }
+    if (p.n_group > 1) {
+      // groups of gsize contiguous experts ranked by the sum of their two
+      // largest fp64 sigmoids (ties to the lower group index); experts of the
+      // other groups are masked
+      const int gsize = E / p.n_group;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (lane + 64 * i < E) wl[lane + 64 * i] = v[i];
+      wave_sync_lds();
+      double score = -1.0;
+      if (lane < p.n_group) {
+        double b1 = -1.0, b2 = -1.0;
+        for (int q = 0; q < gsize; ++q) {
+          double s = 1.0 / (1.0 + exp(-(double)wl[lane * gsize + q]));
+          if (s > b1) { b2 = b1; b1 = s; }
+          else if (s > b2) { b2 = s; }
+        }
+        score = b1 + (gsize > 1 ? b2 : 0.0);
+        L.gscore[wave][lane] = score;
+      }
+      wave_sync_lds();
+      int keep = 0;
+      if (lane < p.n_group) {
+        int rank = 0;
+        for (int g = 0; g < p.n_group; ++g) {
+          double o = L.gscore[wave][g];
+          rank += (o > score || (o == score && g < lane)) ? 1 : 0;
+        }
+        keep = rank < p.topk_group;
+      }
+      const uint64_t keep_mask = __ballot(keep);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        int e = lane + 64 * i;
+        if (e < E && !((keep_mask >> (e / gsize)) & 1ull)) v[i] = -INFINITY;
+      }
+    }
+    // rank = number of experts whose key is larger: keys order by logit, then
+    // by lower expert index; masked experts have key 0 and beat nobody
+    uint64_t kown[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = lane + 64 * i;
+      kown[i] = (e < E && v[i] != -INFINITY) ? order_key(v[i], e) : 0ull;
+      if (e < Epad) wk[e] = kown[i];
+    }
+    wave_sync_lds();
+    int rank[4] = {0, 0, 0, 0};
+    const int nv = (E + 63) >> 6;
+    if (nv == 1)
+      rank_keys<1>(wk, Epad, kown, rank);
+    else if (nv == 2)
+      rank_keys<2>(wk, Epad, kown, rank);
+    else if (nv == 3)
+      rank_keys<3>(wk, Epad, kown, rank);
+    else
+      rank_keys<4>(wk, Epad, kown, rank);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = lane + 64 * i;
+      if (e < E && v[i] != -INFINITY && rank[i] < k) {
+        L.ids[t * k + rank[i]] = e;
+        L.val[t * k + rank[i]] = v[i];
+      }
+    }
+    wave_sync_lds();
+    // weights in fp64: each selected lane forms its term, then sums the k terms
+    // of the token in selection order
+    double full = 0.0;
+    if (p.scoring == 0 && !p.renorm) {
+      const double m = (double)L.val[t * k];   // nothing is masked: the global max
+      double part = 0.0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (lane + 64 * i < E) part += exp((double)v[i] - m);
+      full = wave_sum(part);
+    }
+    double term = 0.0;
+    if (lane < k) {
+      const double mine = (double)L.val[t * k + lane];
+      term = p.scoring == 0 ? exp(mine - (double)L.val[t * k]) : 1.0 / (1.0 + exp(-mine));
+      L.ex[t * k + lane] = term;
+    }
+    wave_sync_lds();
+    if (lane < k) {
+      double den;
+      if (!p.renorm) {
+        den = p.scoring == 0 ? full : 1.0;
+      } else {
+        den = 0.0;
+        for (int j = 0; j < k; ++j) den += L.ex[t * k + j];
+      }
+      L.wts[t * k + lane] = (float)(term / den * (double)p.scale);
+      atomicOr(&L.tokmask[L.ids[t * k + lane]], 1u << t);
+    }
+  }
+  __syncthreads();
+
+  // ---- align: count of expert e = popcount(tokmask[e]); the rank of token t's
+  // slot inside expert e = tokens below t that picked e (slots ascend with t)
+  if (tid < 64) {
+    int pc[4], local = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int e = tid * 4 + i;
+      int c = e < E ? __popc(L.tokmask[e]) : 0;
+      pc[i] = (c + p.bm - 1) / p.bm * p.bm;
+      local += pc[i];
+    }
+    int incl = local;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      int u = __shfl_up(incl, o, 64);
+      if (tid >= o) incl += u;
+    }
+    int run = incl - local;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int e = tid * 4 + i;
+      if (e < E) {
+        L.off[e] = run;
+        if (pc[i] > 0) L.blk_expert[run / p.bm] = e;   // one block per expert (c <= 16 <= bm)
+      }
+      run += pc[i];
+    }
+    if (tid == 63) L.ntpp = incl;
+  }
+  __syncthreads();
+  const int ntpp = L.ntpp;
+  const int b0 = blk >= 0 ? blk * p.bm : -1;
+  for (int s = tid; s < n; s += nthr) {
+    const int e = L.ids[s];
+    const int t = s / k;
+    const int pos = L.off[e] + __popc(L.tokmask[e] & ((1u << t) - 1u));
+    if (b0 >= 0 && pos >= b0 && pos < b0 + 16) L.rowslot[pos - b0] = s;
+    if (write_out) {
+      p.sorted_ids[pos] = s;
+      p.topk_ids[s] = e;
+      p.topk_w[s] = L.wts[s];
+    }
+  }
+  if (write_out) {
+    for (int e = tid; e < E; e += nthr) {
+      int c = __popc(L.tokmask[e]);
+      int pc = (c + p.bm - 1) / p.bm * p.bm;
+      for (int r = c; r < pc; ++r) p.sorted_ids[L.off[e] + r] = n;
+      if (pc > 0) p.expert_ids[L.off[e] / p.bm] = e;
+    }
+    if (tid == 0) *p.ntpp = ntpp;
+  }
+  if (tid == 0) L.my_expert = (blk >= 0 && blk * p.bm < ntpp) ? L.blk_expert[blk] : -1;
+  __syncthreads();
+}
+
+// ------------------------------------------------------------------ GEMV tiles
+// A weight tile is 16 rows x 256 elements (one 512-byte K round per row).  It
+// is loaded with fully coalesced 1 KB wave loads (load j covers tile rows 2j
+// and 2j+1, 32 lanes x 16 bytes each), parked in the wave's own LDS buffer with
+// the 16-byte chunk index XOR-ed by the row, and read back in the MFMA operand
+// layout (lane r + 16 g: row r, chunk 4 q + g for MFMA q), which is then
+// free of bank conflicts.  The token operand uses the same K order:
+// MFMA q covers K elements k0 + 32 q + 8 g + 0..7 for lane group g.
+constexpr int kTileU4 = 16 * 32;   // 16-byte chunks of one tile
+
+// Buffer descriptor over the tile's valid rows (at most 16): loads past them
+// return zero.  DWORD3 0x00020000 = raw 32-bit data format for gfx9 buffers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* first_row, int64_t ld,
+                                                          int rows_valid) {
+  const int rows = rows_valid < 16 ? rows_valid : 16;
+  return __builtin_amdgcn_make_buffer_rsrc((void*)first_row, (short)0, (int)(rows * ld * 2),
+                                           0x00020000);
+}
+
+__device__ __forceinline__ void tile_load(__amdgpu_buffer_rsrc_t rs, int64_t ld, int k0, int K,
+                                          u32x4 (&v)[8]) {
+  const int lane = threadIdx.x & 63;
+  const int kc = k0 + 8 * (lane & 31);
+  const int base = (lane >> 5) * (int)ld * 2 + kc * 2;   // byte offset of row (lane >> 5)
+  const int step = 4 * (int)ld;                          // two rows
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int off = kc < K ? base + j * step : -1;     // -1: beyond the descriptor -> zero
+    v[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 2 /* nontemporal */);
+  }
+}
+
+__device__ __forceinline__ void tile_store(u32x4* lds, const u32x4 (&v)[8]) {
+  const int lane = threadIdx.x & 63;
+  const int ch = lane & 31;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int row = 2 * j + (lane >> 5);
+    lds[row * 32 + (ch ^ row)] = v[j];
+  }
+}
+
+__device__ __forceinline__ u32x4 tile_operand(const u32x4* lds, int q) {
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 15;
+  const int c = 4 * q + (lane >> 4);
+  return lds[r * 32 + (c ^ r)];
+}
+
+__device__ __forceinline__ void token_operands(const uint16_t* row, int k0, int K, u32x4 (&xb)[8]) {
+  const int kg = k0 + 8 * ((threadIdx.x & 63) >> 4);
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
-    int kc = k0 + 8 * q;
-    wa[q] = (w && kc < K) ? *(const u32x4*)(w + kc) : u32x4{0u, 0u, 0u, 0u};
-    xb[q] = (b && kc < K) ? *(const u32x4*)(b + kc) : u32x4{0u, 0u, 0u, 0u};
+    const int kc = kg + 32 * q;
+    xb[q] = (row && kc < K) ? *(const u32x4*)(row + kc) : u32x4{0u, 0u, 0u, 0u};
   }
+}
+
+__device__ __forceinline__ f32x4 tile_mfma(const u32x4* lds, const u32x4 (&xb)[8], f32x4 acc) {
 #pragma unroll
-  for (int q = 0; q < 8; ++q) acc = mfma16(wa[q], xb[q], acc);
+  for (int q = 0; q < 8; ++q) acc = mfma16(tile_operand(lds, q), xb[q], acc);
   return acc;
 }
 
-__device__ __forceinline__ void round16x2(const uint16_t* w0, const uint16_t* w1,
-                                          const uint16_t* b, int k0, int K, f32x4& a0,
-                                          f32x4& a1) {
-  u32x4 wa[8], wb[8], xb[8];
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    int kc = k0 + 8 * q;
-    wa[q] = (w0 && kc < K) ? *(const u32x4*)(w0 + kc) : u32x4{0u, 0u, 0u, 0u};
-    wb[q] = (w1 && kc < K) ? *(const u32x4*)(w1 + kc) : u32x4{0u, 0u, 0u, 0u};
-    xb[q] = (b && kc < K) ? *(const u32x4*)(b + kc) : u32x4{0u, 0u, 0u, 0u};
+// K rounds kp, kp + S, ... of one tile against one token row, with the
+// next round's weight tile requested before the current one is consumed, so
+// that every wave keeps a tile of loads in flight.
+__device__ __forceinline__ f32x4 stream_rounds(__amdgpu_buffer_rsrc_t rs, int K,
+                                               const uint16_t* brow, int kp, int S, int rounds,
+                                               u32x4* tl, f32x4 acc) {
+  u32x4 cur[8], nxt[8], xb[8];
+  int rd = kp;
+  if (rd < rounds) tile_load(rs, K, rd * kRound, K, cur);
+  while (rd < rounds) {
+    const int nrd = rd + S;
+    if (nrd < rounds) tile_load(rs, K, nrd * kRound, K, nxt);
+    token_operands(brow, rd * kRound, K, xb);
+    tile_store(tl, cur);
+    wave_sync_lds();
+    acc = tile_mfma(tl, xb, acc);
+    wave_sync_lds();
+    rd = nrd;
+    if (rd >= rounds) break;
+    const int nrd2 = rd + S;
+    if (nrd2 < rounds) tile_load(rs, K, nrd2 * kRound, K, cur);
+    token_operands(brow, rd * kRound, K, xb);
+    tile_store(tl, nxt);
+    wave_sync_lds();
+    acc = tile_mfma(tl, xb, acc);
+    wave_sync_lds();
+    rd = nrd2;
   }
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    a0 = mfma16(wa[q], xb[q], a0);
-    a1 = mfma16(wb[q], xb[q], a1);
-  }
+  return acc;
 }
 
-// GEMV1: act[row j of block b][c0 + 0..15] = act(x[token j] . w13[e] rows).
-// Grid (ceil(I/16), nblk + shared); 4 waves split K; also zeroes `out`.
+constexpr int kG1Waves = kPrologueWaves;
+constexpr int kG2Waves = 4;
+
+// GEMV1: routing prologue, then the workgroup's p.nt1 tiles of 16 act columns
+// at once, each tile on 8 / p.nt1 waves (SwiGLU: half on the gate rows, half
+// on the up rows) that split K.  act[row j of block b][c0 + 0..15] =
+// act(x[token of row j] . w13[e] rows).  Also zeroes `out`.
+// Grid (ceil(ceil(I/16) / nt1), nblk + shared).
 template <bool SW>
-__global__ void __launch_bounds__(256) gemv1_kernel(GemvParams p) {
-  __shared__ f32x4 s_red[4][2][64];
+__global__ void __launch_bounds__(kG1Waves * 64) gemv1_kernel(GemvParams p) {
+  __shared__ union {
+    RouteLds L;
+    u32x4 tile[kG1Waves][kTileU4];
+  } sm;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
 
-  // zero the output that GEMV2 accumulates into
-  {
+  {  // zero the output that GEMV2 accumulates into
     const int64_t n4 = (int64_t)p.T * p.H / 4;
     const int64_t nwg = (int64_t)gridDim.x * gridDim.y;
     const int64_t wg = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
-    for (int64_t i = wg * 256 + tid; i < n4; i += nwg * 256)
+    for (int64_t i = wg * blockDim.x + tid; i < n4; i += nwg * blockDim.x)
       ((float4*)p.out)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
 
   const int b = blockIdx.y;
-  BlockRows br;
-  br.shared = b == p.nblk;
-  br.base = b * p.bm;
-  const uint16_t* W;
-  if (br.shared) {
-    W = p.sw13;
-  } else {
-    if (br.base >= *p.ntpp) return;
-    int e = p.expert_ids[b];
-    if (e < 0 || e >= p.E) return;
-    W = p.w13 + (int64_t)e * (SW ? 2 * p.I : p.I) * p.H;
-  }
-  const int c0 = blockIdx.x * 16;
-  const int r = lane & 15;   // weight row in the tile / token column
-  const int g = lane >> 4;   // lane group along K
-  int slot;
-  const int tok = block_token(p, br, r, &slot);
+  const bool shared = b == p.nblk;
+  route_prologue(p, sm.L, shared ? -1 : b, blockIdx.x == 0 && blockIdx.y == 0);
+  const int e = sm.L.my_expert;
+  const int r = lane & 15;   // token column of this lane (operand and result)
+  const int g = lane >> 4;
+  const int slot = shared ? (r < p.T ? r : -1) : sm.L.rowslot[r];
+  __syncthreads();           // the LDS union is reused below
+  if (!shared && e < 0) return;
+  const int M1 = SW ? 2 * p.I : p.I;
+  const uint16_t* W = shared ? p.sw13 : p.w13 + (int64_t)e * M1 * p.H;
+  const int tok = slot < 0 ? -1 : (shared ? slot : slot / p.k);
   const uint16_t* xrow = tok >= 0 ? p.x + (int64_t)tok * p.H : nullptr;
-  const bool rowok = c0 + r < p.I;
-  const uint16_t* wg_row = rowok ? W + (int64_t)(c0 + r) * p.H : nullptr;
-  const uint16_t* wu_row = (SW && rowok) ? W + (int64_t)(p.I + c0 + r) * p.H : nullptr;
-
-  f32x4 ag = {0.f, 0.f, 0.f, 0.f}, au = {0.f, 0.f, 0.f, 0.f};
+  u32x4* tl = sm.tile[wave];
   const int rounds = (p.H + kRound - 1) / kRound;
-  for (int rd = wave; rd < rounds; rd += 4) {
-    const int k0 = rd * kRound + 64 * g;
-    if (SW)
-      round16x2(wg_row, wu_row, xrow, k0, p.H, ag, au);
-    else
-      ag = round16(wg_row, xrow, k0, p.H, ag);
+
+  // tile ti of the workgroup is handled by `per` waves: SwiGLU gives half of
+  // them the gate rows and half the up rows, each half splitting K S ways
+  const int per = kG1Waves / p.nt1;
+  const int S = SW ? per / 2 : per;
+  const int ti = wave / per;
+  const int wi = wave % per;
+  const bool up = SW && wi >= S;
+  const int kp = wi % S;
+  const int c0 = (blockIdx.x * p.nt1 + ti) * 16;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (c0 < p.I) {
+    const __amdgpu_buffer_rsrc_t rs =
+        tile_rsrc(W + (int64_t)((up ? p.I : 0) + c0) * p.H, p.H, p.I - c0);
+    acc = stream_rounds(rs, p.H, xrow, kp, S, rounds, tl, acc);
   }
-  s_red[wave][0][lane] = ag;
-  if (SW) s_red[wave][1][lane] = au;
+  ((f32x4*)tl)[lane] = acc;   // partial sums reuse the wave's own tile buffer
   __syncthreads();
-  if (wave != 0) return;
-  f32x4 hg = s_red[0][0][lane], hu = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int w = 1; w < 4; ++w) hg += s_red[w][0][lane];
-  if (SW) {
-    hu = s_red[0][1][lane];
-#pragma unroll
-    for (int w = 1; w < 4; ++w) hu += s_red[w][1][lane];
+  if (wi != 0 || c0 >= p.I || slot < 0 || c0 + 4 * g >= p.I) return;
+  f32x4 hg = acc, hu = {0.f, 0.f, 0.f, 0.f};
+  for (int w = 1; w < per; ++w) {
+    const f32x4 o = ((const f32x4*)sm.tile[wave + w])[lane];
+    if (SW && w >= S) hu += o; else hg += o;
   }
-  // lane holds rows (act cols) c0 + 4g + v of token column j = lane & 15
-  const int j = lane & 15;
-  int slot_j;
-  const int tok_j = block_token(p, br, j, &slot_j);
-  if (tok_j < 0) return;
-  const int col = c0 + 4 * g;
-  if (col >= p.I) return;
-  float o[4];
+  // lane holds act columns c0 + 4 g + v of token column r
+  float o4[4];
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     if (SW) {
-      o[v] = silu(hg[v]) * hu[v];
+      o4[v] = silu(hg[v]) * hu[v];
     } else {
       float t = fmaxf(hg[v], 0.f);
-      o[v] = t * t;
+      o4[v] = t * t;
     }
   }
-  uint16_t* dst = br.shared ? p.act_sh + (int64_t)j * p.I : p.act + (int64_t)(br.base + j) * p.I;
+  uint16_t* dst = shared ? p.act_sh + (int64_t)r * p.I : p.act + (int64_t)(b * p.bm + r) * p.I;
   uint2 pk;
-  pk.x = (unsigned)f32_to_bf16(o[0]) | ((unsigned)f32_to_bf16(o[1]) << 16);
-  pk.y = (unsigned)f32_to_bf16(o[2]) | ((unsigned)f32_to_bf16(o[3]) << 16);
-  *(uint2*)(dst + col) = pk;
+  pk.x = (unsigned)f32_to_bf16(o4[0]) | ((unsigned)f32_to_bf16(o4[1]) << 16);
+  pk.y = (unsigned)f32_to_bf16(o4[2]) | ((unsigned)f32_to_bf16(o4[3]) << 16);
+  *(uint2*)(dst + c0 + 4 * g) = pk;
 }
 
-// GEMV2: out[token j][h] += w_slot * (act[row j] . w2[e][h]) for 16 rows h per
-// wave.  Grid (ceil(H/64), nblk + shared).
-__global__ void __launch_bounds__(256) gemv2_kernel(GemvParams p) {
+// GEMV2: the workgroup's p.nt2 tiles of 16 output rows at once, each on
+// p.s2 = 4 / p.nt2 waves that split K; out[token of row j][h0 + ..] +=
+// w_slot * (act[row j] . w2[e][h]).  Grid (ceil(ceil(H/16) / nt2), nblk + shared).
+__global__ void __launch_bounds__(kG2Waves * 64) gemv2_kernel(GemvParams p) {
+  __shared__ u32x4 s_tile[kG2Waves][kTileU4];
+  __shared__ int s_slot[16];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int b = blockIdx.y;
-  BlockRows br;
-  br.shared = b == p.nblk;
-  br.base = b * p.bm;
+  const bool shared = b == p.nblk;
+  const int base = b * p.bm;
   const uint16_t* W;
-  if (br.shared) {
+  if (shared) {
     W = p.sw2;
   } else {
-    if (br.base >= *p.ntpp) return;
-    int e = p.expert_ids[b];
+    if (base >= *p.ntpp) return;
+    const int e = p.expert_ids[b];
     if (e < 0 || e >= p.E) return;
     W = p.w2 + (int64_t)e * p.H * p.I;
   }
-  const int h0 = (blockIdx.x * 4 + wave) * 16;
-  if (h0 >= p.H) return;
+  if (tid < 16) {
+    int s = -1;
+    if (shared) {
+      s = tid < p.T ? tid : -1;
+    } else {
+      int sid = p.sorted_ids[base + tid];
+      s = (sid >= 0 && sid < p.T * p.k) ? sid : -1;
+    }
+    s_slot[tid] = s;
+  }
+  __syncthreads();
   const int r = lane & 15;
   const int g = lane >> 4;
-  int slot;
-  const int tok = block_token(p, br, r, &slot);
+  const int slot = s_slot[r];
   const uint16_t* arow = nullptr;
-  if (tok >= 0)
-    arow = br.shared ? p.act_sh + (int64_t)r * p.I : p.act + (int64_t)(br.base + r) * p.I;
-  const uint16_t* wrow = h0 + r < p.H ? W + (int64_t)(h0 + r) * p.I : nullptr;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (slot >= 0) arow = shared ? p.act_sh + (int64_t)r * p.I : p.act + (int64_t)(base + r) * p.I;
+  u32x4* tl = s_tile[wave];
   const int rounds = (p.I + kRound - 1) / kRound;
-  for (int rd = 0; rd < rounds; ++rd) acc = round16(wrow, arow, rd * kRound + 64 * g, p.I, acc);
-  // lane holds rows h0 + 4g + v of token column j = lane & 15
-  const int j = lane & 15;
-  int slot_j;
-  const int tok_j = block_token(p, br, j, &slot_j);
-  if (tok_j < 0) return;
-  const float wgt = br.shared ? 1.f : p.topk_w[slot_j];
-  float* dst = p.out + (int64_t)tok_j * p.H + h0 + 4 * g;
+
+  const int S = kG2Waves / p.nt2;
+  const int ti = wave / S;
+  const int kp = wave % S;
+  const int h0 = (blockIdx.x * p.nt2 + ti) * 16;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (h0 < p.H) {
+    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(W + (int64_t)h0 * p.I, p.I, p.H - h0);
+    acc = stream_rounds(rs, p.I, arow, kp, S, rounds, tl, acc);
+  }
+  ((f32x4*)tl)[lane] = acc;
+  __syncthreads();
+  if (kp != 0 || h0 >= p.H || slot < 0) return;
+  for (int w = wave + 1; w < wave + S; ++w) acc += ((const f32x4*)s_tile[w])[lane];
+  const int tok = shared ? slot : slot / p.k;
+  const float wgt = shared ? 1.f : p.topk_w[slot];
+  // lane holds rows h0 + 4 g + v of token column r
+  float* dst = p.out + (int64_t)tok * p.H + h0 + 4 * g;
 #pragma unroll
   for (int v = 0; v < 4; ++v)
     if (h0 + 4 * g + v < p.H) unsafeAtomicAdd(dst + v, wgt * acc[v]);
@@ -231,16 +537,28 @@ __global__ void __launch_bounds__(256) gemv2_kernel(GemvParams p) {
 
 }  // namespace
 
-hipError_t launch_gemv(const GemvParams& p, bool swiglu, hipStream_t s) {
-  const unsigned nb = (unsigned)(p.nblk + (p.sw13 ? 1 : 0));
-  if (nb == 0) return hipSuccess;
-  dim3 g1((p.I + 15) / 16, nb);
+// Tiles per workgroup: the largest power of two (up to the wave count) that
+// still leaves about two workgroups per CU; the remaining waves split K.
+static int pick_tiles(int64_t tiles, int waves, int64_t target) {
+  int nt = 1;
+  while (nt < waves && tiles / (2 * nt) >= target) nt *= 2;
+  return nt;
+}
+
+hipError_t launch_gemv(const GemvParams& p0, bool swiglu, hipStream_t s) {
+  GemvParams p = p0;
+  const int nb = p.nblk + (p.sw13 ? 1 : 0);
+  const int tiles1 = (p.I + 15) / 16;
+  const int tiles2 = (p.H + 15) / 16;
+  p.nt1 = pick_tiles((int64_t)tiles1 * nb, swiglu ? kG1Waves / 2 : kG1Waves, 768);
+  p.nt2 = pick_tiles((int64_t)tiles2 * nb, kG2Waves, 768);
+  dim3 g1((tiles1 + p.nt1 - 1) / p.nt1, nb);
   if (swiglu)
-    hipLaunchKernelGGL(gemv1_kernel<true>, g1, dim3(256), 0, s, p);
+    hipLaunchKernelGGL(gemv1_kernel<true>, g1, dim3(kG1Waves * 64), 0, s, p);
   else
-    hipLaunchKernelGGL(gemv1_kernel<false>, g1, dim3(256), 0, s, p);
-  dim3 g2((p.H + 63) / 64, nb);
-  hipLaunchKernelGGL(gemv2_kernel, g2, dim3(256), 0, s, p);
+    hipLaunchKernelGGL(gemv1_kernel<false>, g1, dim3(kG1Waves * 64), 0, s, p);
+  dim3 g2((tiles2 + p.nt2 - 1) / p.nt2, nb);
+  hipLaunchKernelGGL(gemv2_kernel, g2, dim3(kG2Waves * 64), 0, s, p);
   return hipGetLastError();
 }
 

@@ -9,7 +9,7 @@
 #include <cmath>
 #include <cstring>
 
-#include "../../include/moe.h"
+#include "moe.h"
 #include "moe_internal.h"
 
 namespace {
@@ -263,6 +263,39 @@ int moe_fused_forward(const moe_layer_params* p, const void* x, const float* rou
   int32_t* eids = expert_ids ? expert_ids : L.expert_ids;
   int32_t* ntpp = num_tokens_post_padded ? num_tokens_post_padded : L.ntpp;
 
+  // ---- decode shapes: routing folded into the first of two expert GEMVs,
+  // each touched expert's weights read once
+  if (T <= moe::kGemvMaxTokens) {
+    moe::GemvParams gv{};
+    gv.x = (const uint16_t*)x;
+    gv.logits = router_logits;
+    gv.w13 = (const uint16_t*)w13;
+    gv.w2 = (const uint16_t*)w2;
+    gv.sw13 = p->n_shared ? (const uint16_t*)shared_w13 : nullptr;
+    gv.sw2 = p->n_shared ? (const uint16_t*)shared_w2 : nullptr;
+    gv.topk_ids = ids;
+    gv.topk_w = wts;
+    gv.sorted_ids = sorted;
+    gv.expert_ids = eids;
+    gv.ntpp = ntpp;
+    gv.T = T;
+    gv.H = H;
+    gv.I = I;
+    gv.k = k;
+    gv.E = E;
+    gv.bm = bm;
+    gv.nblk = (int)(n < E ? n : E);
+    gv.scoring = p->scoring;
+    gv.n_group = p->n_group;
+    gv.topk_group = p->topk_group;
+    gv.renorm = p->renormalize;
+    gv.scale = p->routed_scaling_factor;
+    gv.act = L.act;
+    gv.act_sh = L.act_sh;
+    gv.out = out;
+    return hip_status(moe::launch_gemv(gv, p->activation == MOE_ACT_SWIGLU, s));
+  }
+
   // ---- routing
   moe::GateParams g{};
   g.logits = router_logits;
@@ -285,31 +318,6 @@ int moe_fused_forward(const moe_layer_params* p, const void* x, const float* rou
     if (e == hipSuccess) e = moe::launch_align(a, s);
   }
   if (e != hipSuccess) return hip_status(e);
-
-  // ---- decode shapes: expert GEMVs, each touched expert's weights read once
-  if (T <= moe::kGemvMaxTokens) {
-    moe::GemvParams gv{};
-    gv.x = (const uint16_t*)x;
-    gv.w13 = (const uint16_t*)w13;
-    gv.w2 = (const uint16_t*)w2;
-    gv.sw13 = p->n_shared ? (const uint16_t*)shared_w13 : nullptr;
-    gv.sw2 = p->n_shared ? (const uint16_t*)shared_w2 : nullptr;
-    gv.sorted_ids = sorted;
-    gv.expert_ids = eids;
-    gv.ntpp = ntpp;
-    gv.topk_w = wts;
-    gv.T = T;
-    gv.H = H;
-    gv.I = I;
-    gv.k = k;
-    gv.E = E;
-    gv.bm = bm;
-    gv.nblk = (int)(n < E ? n : E);
-    gv.act = L.act;
-    gv.act_sh = L.act_sh;
-    gv.out = out;
-    return hip_status(moe::launch_gemv(gv, p->activation == MOE_ACT_SWIGLU, s));
-  }
 
   // ---- GEMM1 + activation: act[i] = act(x[sorted[i] / k] . w13[e]^T)
   const int epi1 = p->activation == MOE_ACT_SWIGLU ? MOE_EPI_SWIGLU : MOE_EPI_RELU2;

@@ -8,6 +8,8 @@
 
 namespace moe {
 
+constexpr int kMaxExperts = 256;
+
 // ---------------------------------------------------------------- gating
 struct GateParams {
   const float* logits;  // [T, E]
@@ -63,16 +65,22 @@ constexpr int kGemvMaxTokens = 16;     // T at or below this takes the GEMV path
 
 struct GemvParams {
   const uint16_t* x;        // [T, H]
+  const float* logits;      // [T, E]
   const uint16_t* w13;      // [E, M1, H]
   const uint16_t* w2;       // [E, H, I]
   const uint16_t* sw13;     // shared expert [M1, H] or null
   const uint16_t* sw2;      // shared expert [H, I] or null
-  const int* sorted_ids;
-  const int* expert_ids;
-  const int* ntpp;
-  const float* topk_w;      // [T * k]
+  // routing outputs: written by GEMV1's workgroup (0,0), read by GEMV2
+  int* topk_ids;            // [T * k]
+  float* topk_w;            // [T * k]
+  int* sorted_ids;          // [capacity]
+  int* expert_ids;          // [capacity / bm]
+  int* ntpp;                // [1]
   int T, H, I, k, E, bm;
   int nblk;                 // routed blocks that can exist: min(E, T * k)
+  int scoring, n_group, topk_group, renorm;
+  float scale;
+  int nt1, nt2;             // 16-row tiles per workgroup of GEMV1 / GEMV2 (set by the launcher)
   uint16_t* act;            // [capacity, I] rows in padded order
   uint16_t* act_sh;         // [T, I]
   float* out;               // [T, H], zeroed by GEMV1, accumulated by GEMV2
