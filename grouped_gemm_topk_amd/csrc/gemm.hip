@@ -14,9 +14,14 @@
 // C^T = W_e . X^T: the weight rows play the MFMA "A" role and the gathered
 // token rows the "B" role, so each lane ends up owning 4 consecutive output
 // features of one token row and stores them as one 8- or 16-byte write.
-// Operands are staged global -> registers -> LDS (double buffered, one barrier
-// per 64-wide K step).  LDS rows are 128 bytes with the 16-byte chunk index
-// XOR-swizzled by the row so that the MFMA operand reads spread over banks.
+// Operands are staged global -> registers -> LDS: buffer loads run NS K steps
+// ahead of the MFMAs in register stages, LDS is double buffered with one
+// barrier per K step, and the LDS chunk order is XOR-swizzled so MFMA operand
+// reads and the stores are free of bank conflicts.  Workgroups are mapped to
+// tiles XCD by XCD (each XCD gets a contiguous tile range) and, inside a
+// range, in groups of 8 M-blocks per N-tile so that a weight tile is reused
+// from that XCD's L2 (the L2 grouping / cache-aware scheduling of the skill
+// card's *Optimization Patterns*).
 // v_mfma_f32_32x32x16_bf16 is used when a wave owns >= 32 token rows,
 // v_mfma_f32_16x16x32_bf16 for BLOCK_M = 16.
 #include <hip/hip_runtime.h>
@@ -32,7 +37,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int BK = 64;
+
 
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   unsigned u = __float_as_uint(f);
@@ -49,7 +54,6 @@ struct Mfma;
 template <>
 struct Mfma<32> {
   typedef f32x16 acc_t;
-  static constexpr int kSteps = BK / 16;  // k per instruction: 16
   static constexpr int kVals = 16;
   __device__ static __forceinline__ acc_t run(bf16x8 a, bf16x8 b, acc_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -66,7 +70,6 @@ struct Mfma<32> {
 template <>
 struct Mfma<16> {
   typedef f32x4 acc_t;
-  static constexpr int kSteps = BK / 32;  // k per instruction: 32
   static constexpr int kVals = 4;
   __device__ static __forceinline__ acc_t run(bf16x8 a, bf16x8 b, acc_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -78,27 +81,54 @@ struct Mfma<16> {
   static constexpr int kGroups = 1;
 };
 
-__device__ __forceinline__ int swz(int r, int c) { return r * 8 + (c ^ (r & 7)); }
+// Operand tiles live in LDS as rows of BK bf16 (CPR = BK / 8 chunks of 16
+// bytes).  16 / CPR rows fill the 64 banks once; XOR-ing the chunk with
+// (row / (16 / CPR)) mod CPR gives any 16 consecutive rows read at one chunk
+// 16 distinct bank groups, and 16 consecutive threads writing consecutive
+// chunks hit distinct ones too.
+template <int CPR>
+__device__ __forceinline__ int swz(int r, int c) {
+  return r * CPR + (c ^ ((r / (16 / CPR)) % CPR));
+}
 
-// BM token rows x BNW weight rows per workgroup tile; WAVES_M x WAVES_N waves.
+// Buffer descriptor (gfx9 raw buffer, 32-bit data) over `bytes` bytes; a load
+// whose offset is at or beyond `bytes` returns zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ int xcd_tile(int L, int n) {
+  // workgroups are handed to the 8 XCDs round-robin by linear id: give XCD x
+  // the contiguous tile range [start(x), start(x + 1))
+  const int q = n >> 3, r = n & 7, x = L & 7;
+  return x * q + (x < r ? x : r) + (L >> 3);
+}
+
+// BM token rows x BNW weight rows per workgroup tile, WAVES_M x WAVES_N waves,
+// BK-wide K steps, NS register stages of global prefetch (loads for step
+// kt + NS are issued while step kt is computed), MINW waves per SIMD.
 // SW: the tile's first BNW/2 weight rows are gate rows n0.., the rest the up
 // rows I+n0.. of the same act columns, and the epilogue is SwiGLU.
-template <int BM, int BNW, int WAVES_M, int WAVES_N, bool SW>
-__global__ void __launch_bounds__(256) grouped_gemm_kernel(GemmParams p) {
+template <int BM, int BNW, int WAVES_M, int WAVES_N, bool SW, int BK, int NS, int MINW>
+__global__ void __launch_bounds__(256, MINW) grouped_gemm_kernel(GemmParams p) {
+  constexpr int CPR = BK / 8;
   constexpr int WM = BM / WAVES_M;
   constexpr int MT = WM >= 32 ? 32 : 16;
   typedef Mfma<MT> M;
+  constexpr int KSTEPS = BK / (MT == 32 ? 16 : 32);
   constexpr int WNW = BNW / WAVES_N;
   constexpr int FM = WM / MT;
   constexpr int FN = WNW / MT;
-  constexpr int XL = (BM * 8 + 255) / 256;
-  constexpr int WL = BNW * 8 / 256;
+  constexpr int XL = (BM * CPR + 255) / 256;
+  constexpr int WL = BNW * CPR / 256;
   static_assert(WAVES_M * WAVES_N == 4, "4 waves");
   static_assert(!SW || FN % 2 == 0, "SwiGLU pairs gate and up subtiles");
-  static_assert(BNW * 8 % 256 == 0, "weight tile load");
+  static_assert(BNW * CPR % 256 == 0, "weight tile load");
+  static_assert(KSTEPS >= 1, "K step");
 
-  __shared__ u32x4 sX[2][BM * 8];
-  __shared__ u32x4 sW[2][BNW * 8];
+  constexpr int NBUF = 3;
+  __shared__ u32x4 sX[NBUF][BM * CPR];
+  __shared__ u32x4 sW[NBUF][BNW * CPR];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -106,7 +136,16 @@ __global__ void __launch_bounds__(256) grouped_gemm_kernel(GemmParams p) {
   const int wn = wave % WAVES_N;
   const int wm = wave / WAVES_N;
 
-  const int mb = blockIdx.y;
+  // ---- tile of this workgroup: XCD-contiguous, groups of GM m-blocks per n-tile
+  const int ntn = p.ntiles_n, nmb = p.mblocks;
+  const int t = xcd_tile(blockIdx.x, ntn * nmb);
+  constexpr int GM = 8;
+  const int grp = t / (GM * ntn);
+  const int gsz = min(GM, nmb - grp * GM);
+  const int j = t - grp * GM * ntn;
+  const int mb = grp * GM + j % gsz;
+  const int nt = j / gsz;
+
   const int m0 = mb * BM;
   const int total_rows = p.ntpp ? *p.ntpp : p.M;
   if (m0 >= total_rows) return;
@@ -114,50 +153,70 @@ __global__ void __launch_bounds__(256) grouped_gemm_kernel(GemmParams p) {
   if (e < 0 || e >= p.E) return;
   const uint16_t* We = p.W + (int64_t)e * p.N * p.K;
   const int ncols = SW ? p.I : p.N;           // output columns
-  const int n0 = blockIdx.x * (SW ? BNW / 2 : BNW);
+  const int n0 = nt * (SW ? BNW / 2 : BNW);
+  const __amdgpu_buffer_rsrc_t xr_rs = make_rsrc(p.A, (int64_t)p.a_rows * p.K * 2);
+  const __amdgpu_buffer_rsrc_t wr_rs = make_rsrc(We, (int64_t)p.N * p.K * 2);
 
-  // ---- per-thread global source rows (null = zero row)
-  const uint16_t* xsrc[XL];
-  int xch[XL], xrow[XL];
+  // ---- per-thread byte offsets of the source rows; kNoRow (beyond every
+  // descriptor even after the K advance is added) reads zeros
+  constexpr int kNoRow = 0x7fff0000;
+  int xoff[XL], xsa[XL], xch[XL];
 #pragma unroll
-  for (int j = 0; j < XL; ++j) {
-    int idx = tid + 256 * j;
-    xrow[j] = idx >> 3;
-    xch[j] = idx & 7;
-    xsrc[j] = nullptr;
-    if (idx < BM * 8) {
-      int i = m0 + xrow[j];
+  for (int q = 0; q < XL; ++q) {
+    const int idx = tid + 256 * q;
+    const int row = idx / CPR;
+    xch[q] = idx % CPR;
+    xsa[q] = swz<CPR>(row, xch[q]);
+    xoff[q] = kNoRow;
+    if (idx < BM * CPR) {
+      const int i = m0 + row;
+      int arow = -1;
       if (p.sorted_ids) {
-        int sid = p.sorted_ids[i];
-        if (sid >= 0 && sid < p.num_valid) {
-          int arow = p.a_row_div ? sid / p.a_row_div : i;
-          xsrc[j] = p.A + (int64_t)arow * p.K;
-        }
+        const int sid = p.sorted_ids[i];
+        if (sid >= 0 && sid < p.num_valid) arow = p.a_row_div ? sid / p.a_row_div : i;
       } else if (i < p.M) {
-        xsrc[j] = p.A + (int64_t)i * p.K;
+        arow = i;
       }
+      if (arow >= 0) xoff[q] = arow * p.K * 2 + xch[q] * 16;
     }
   }
-  const uint16_t* wsrc[WL];
-  int wch[WL], wrow[WL];
+  int woff[WL], wsa[WL], wch[WL];
 #pragma unroll
-  for (int j = 0; j < WL; ++j) {
-    int idx = tid + 256 * j;
-    int r = idx >> 3;
-    wrow[j] = r;
-    wch[j] = idx & 7;
+  for (int q = 0; q < WL; ++q) {
+    const int idx = tid + 256 * q;
+    const int r = idx / CPR;
+    wch[q] = idx % CPR;
+    wsa[q] = swz<CPR>(r, wch[q]);
     int g;
     bool ok;
     if (SW) {
-      int c = r < BNW / 2 ? n0 + r : n0 + r - BNW / 2;
+      const int c = r < BNW / 2 ? n0 + r : n0 + r - BNW / 2;
       ok = c < p.I;
       g = r < BNW / 2 ? c : p.I + c;
     } else {
       g = n0 + r;
       ok = g < p.N;
     }
-    wsrc[j] = ok ? We + (int64_t)g * p.K : nullptr;
+    woff[q] = ok ? g * p.K * 2 + wch[q] * 16 : kNoRow;
   }
+
+  // ---- LDS read addresses: every operand row a lane reads is row(lane) plus
+  // a multiple of 16, which keeps the swizzle mask of row(lane); so per
+  // k-substep one base index per operand and compile-time subtile offsets
+  constexpr int WNA = SW ? BNW / 2 / WAVES_N : WNW;
+  int xb[KSTEPS], wb[KSTEPS];
+#pragma unroll
+  for (int kk = 0; kk < KSTEPS; ++kk) {
+    const int lr = M::row(lane);
+    const int lb = swz<CPR>(lr, M::chunk(kk, lane));
+    xb[kk] = lb + wm * WM * CPR;
+    wb[kk] = lb + wn * WNA * CPR;
+  }
+  // weight subtile f starts this many rows after the wave's first weight row
+  auto wsub_off = [&](int f) {
+    if (SW) return f < FN / 2 ? f * MT : BNW / 2 + (f - FN / 2) * MT;
+    return f * MT;
+  };
 
   typename M::acc_t acc[FN][FM];
 #pragma unroll
@@ -168,67 +227,85 @@ __global__ void __launch_bounds__(256) grouped_gemm_kernel(GemmParams p) {
       for (int v = 0; v < M::kVals; ++v) acc[f][q][v] = 0.f;
 
   u32x4 xr[XL], wr[WL];
+  // loads of K step kt: the K advance rides in the scalar offset
   auto gload = [&](int kt) {
+    const int k0b = kt * BK * 2;
+#pragma unroll
+    for (int q = 0; q < XL; ++q) xr[q] = __builtin_amdgcn_raw_buffer_load_b128(xr_rs, xoff[q], k0b, 0);
+#pragma unroll
+    for (int q = 0; q < WL; ++q) wr[q] = __builtin_amdgcn_raw_buffer_load_b128(wr_rs, woff[q], k0b, 0);
+  };
+  // the last K step when K % BK != 0: chunks past K read zeros
+  auto gload_tail = [&](int kt) {
     const int k0 = kt * BK;
 #pragma unroll
-    for (int j = 0; j < XL; ++j) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      int kc = k0 + xch[j] * 8;
-      if (xsrc[j] && kc < p.K) v = *(const u32x4*)(xsrc[j] + kc);
-      xr[j] = v;
+    for (int q = 0; q < XL; ++q) {
+      const int off = k0 + xch[q] * 8 < p.K ? xoff[q] + k0 * 2 : kNoRow;
+      xr[q] = __builtin_amdgcn_raw_buffer_load_b128(xr_rs, off, 0, 0);
     }
 #pragma unroll
-    for (int j = 0; j < WL; ++j) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      int kc = k0 + wch[j] * 8;
-      if (wsrc[j] && kc < p.K) v = *(const u32x4*)(wsrc[j] + kc);
-      wr[j] = v;
+    for (int q = 0; q < WL; ++q) {
+      const int off = k0 + wch[q] * 8 < p.K ? woff[q] + k0 * 2 : kNoRow;
+      wr[q] = __builtin_amdgcn_raw_buffer_load_b128(wr_rs, off, 0, 0);
     }
   };
-  auto sstore = [&](int buf) {
+  auto sstore = [&](u32x4* sx, u32x4* sw) {
 #pragma unroll
-    for (int j = 0; j < XL; ++j)
-      if (tid + 256 * j < BM * 8) sX[buf][swz(xrow[j], xch[j])] = xr[j];
+    for (int q = 0; q < XL; ++q)
+      if (tid + 256 * q < BM * CPR) sx[xsa[q]] = xr[q];
 #pragma unroll
-    for (int j = 0; j < WL; ++j) sW[buf][swz(wrow[j], wch[j])] = wr[j];
+    for (int q = 0; q < WL; ++q) sw[wsa[q]] = wr[q];
   };
-  // local weight row of subtile f of this wave
-  auto wsub = [&](int f) {
-    if (SW) {
-      constexpr int WNA = BNW / 2 / WAVES_N;
-      return f < FN / 2 ? wn * WNA + f * MT : BNW / 2 + wn * WNA + (f - FN / 2) * MT;
-    }
-    return wn * WNW + f * MT;
+  // operand registers of one k-substep
+  struct Ops {
+    bf16x8 b[FM], a[FN];
+  };
+  auto read_ops = [&](const u32x4* sx, const u32x4* sw, int kk, Ops& o) {
+#pragma unroll
+    for (int q = 0; q < FM; ++q) o.b[q] = __builtin_bit_cast(bf16x8, sx[xb[kk] + q * MT * CPR]);
+#pragma unroll
+    for (int f = 0; f < FN; ++f) o.a[f] = __builtin_bit_cast(bf16x8, sw[wb[kk] + wsub_off(f) * CPR]);
+  };
+  auto mfmas = [&](const Ops& o) {
+#pragma unroll
+    for (int f = 0; f < FN; ++f)
+#pragma unroll
+      for (int q = 0; q < FM; ++q) acc[f][q] = M::run(o.a[f], o.b[q], acc[f][q]);
   };
 
+  // ---- pipeline over K steps with three LDS buffers and one barrier per step.
+  // Step kt: store step kt + 1 (loaded during step kt - 1) into buffer
+  // (kt + 1) % 3, request step kt + 2, barrier (step kt + 1 is now visible and
+  // every wave is done reading buffer (kt + 2) % 3), then the MFMAs of step kt
+  // with each k-substep's operands read one substep ahead; the first
+  // substep of step kt + 1 is read during the last MFMAs of step kt.
   const int nk = (p.K + BK - 1) / BK;
-  gload(0);
-  sstore(0);
+  const bool ktail = p.K % BK != 0;
+  auto load_step = [&](int kt) {
+    if (ktail && kt == nk - 1) gload_tail(kt); else gload(kt);
+  };
+  load_step(0);
+  sstore(sX[0], sW[0]);
+  if (nk > 1) load_step(1);
   __syncthreads();
+  Ops cur, nxt;
+  read_ops(sX[0], sW[0], 0, cur);
+  int b0 = 0;   // buffer of step kt
   for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-#pragma unroll
-    for (int kk = 0; kk < M::kSteps; ++kk) {
-      const int c = M::chunk(kk, lane);
-      bf16x8 bx[FM];
-#pragma unroll
-      for (int q = 0; q < FM; ++q) {
-        int r = wm * WM + q * MT + M::row(lane);
-        u32x4 t = sX[buf][swz(r, c)];
-        bx[q] = __builtin_bit_cast(bf16x8, t);
-      }
-#pragma unroll
-      for (int f = 0; f < FN; ++f) {
-        int r = wsub(f) + M::row(lane);
-        u32x4 t = sW[buf][swz(r, c)];
-        bf16x8 aw = __builtin_bit_cast(bf16x8, t);
-#pragma unroll
-        for (int q = 0; q < FM; ++q) acc[f][q] = M::run(aw, bx[q], acc[f][q]);
-      }
-    }
-    if (kt + 1 < nk) sstore(buf ^ 1);
+    const int b1 = b0 == NBUF - 1 ? 0 : b0 + 1;
+    if (kt + 1 < nk) sstore(sX[b1], sW[b1]);
+    if (kt + 2 < nk) load_step(kt + 2);
     __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+      if (kk + 1 < KSTEPS)
+        read_ops(sX[b0], sW[b0], kk + 1, nxt);
+      else if (kt + 1 < nk)
+        read_ops(sX[b1], sW[b1], 0, nxt);
+      mfmas(cur);
+      cur = nxt;
+    }
+    b0 = b1;
   }
 
   // ---- epilogue
@@ -267,12 +344,12 @@ __global__ void __launch_bounds__(256) grouped_gemm_kernel(GemmParams p) {
         float o[4];
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          float h = acc[f][q][4 * g + v];
+          const float h = acc[f][q][4 * g + v];
           if (SW) {
-            float u = acc[f + FN / 2][q][4 * g + v];
+            const float u = acc[f + FN / 2][q][4 * g + v];
             o[v] = silu(h) * u;
           } else if (epi == 2) {
-            float r = fmaxf(h, 0.f);
+            const float r = fmaxf(h, 0.f);
             o[v] = r * r;
           } else {
             o[v] = h * scale;
@@ -292,31 +369,46 @@ __global__ void __launch_bounds__(256) grouped_gemm_kernel(GemmParams p) {
   }
 }
 
-template <int BM, int BNW, int WAVES_M, int WAVES_N>
-hipError_t launch_bm(const GemmParams& p, hipStream_t s) {
+template <int BM, int BNW, int WAVES_M, int WAVES_N, int BK, int NS, int MINW>
+hipError_t launch_bm(GemmParams p, hipStream_t s) {
   const bool sw = p.epi == 1;
   const int ncols = sw ? p.I : p.N;
   const int tile_n = sw ? BNW / 2 : BNW;
-  const int mblocks = (p.M + BM - 1) / BM;
-  dim3 grid((ncols + tile_n - 1) / tile_n, mblocks);
-  if (grid.x == 0 || grid.y == 0) return hipSuccess;
+  p.mblocks = (p.M + BM - 1) / BM;
+  p.ntiles_n = (ncols + tile_n - 1) / tile_n;
+  const int64_t nwg = (int64_t)p.mblocks * p.ntiles_n;
+  if (nwg == 0) return hipSuccess;
   if (sw)
-    hipLaunchKernelGGL((grouped_gemm_kernel<BM, BNW, WAVES_M, WAVES_N, true>), grid, dim3(256), 0,
-                       s, p);
+    hipLaunchKernelGGL((grouped_gemm_kernel<BM, BNW, WAVES_M, WAVES_N, true, BK, NS, MINW>),
+                       dim3((unsigned)nwg), dim3(256), 0, s, p);
   else
-    hipLaunchKernelGGL((grouped_gemm_kernel<BM, BNW, WAVES_M, WAVES_N, false>), grid, dim3(256),
-                       0, s, p);
+    hipLaunchKernelGGL((grouped_gemm_kernel<BM, BNW, WAVES_M, WAVES_N, false, BK, NS, MINW>),
+                       dim3((unsigned)nwg), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
+// Tile configurations per BLOCK_M (compile-time knobs, defaults tuned on MI355X).
+#ifndef MOE_G128
+#define MOE_G128 128, 256, 2, 2, 32, 1, 2
+#endif
+#ifndef MOE_G64
+#define MOE_G64 64, 256, 1, 4, 64, 2, 1
+#endif
+#ifndef MOE_G32
+#define MOE_G32 32, 256, 1, 4, 64, 2, 1
+#endif
+#ifndef MOE_G16
+#define MOE_G16 16, 128, 1, 4, 64, 2, 2
+#endif
+
 hipError_t launch_grouped_gemm(const GemmParams& p, int block_m, hipStream_t s) {
   switch (block_m) {
-    case 128: return launch_bm<128, 256, 2, 2>(p, s);
-    case 64: return launch_bm<64, 256, 1, 4>(p, s);
-    case 32: return launch_bm<32, 256, 1, 4>(p, s);
-    case 16: return launch_bm<16, 128, 1, 4>(p, s);
+    case 128: return launch_bm<MOE_G128>(p, s);
+    case 64: return launch_bm<MOE_G64>(p, s);
+    case 32: return launch_bm<MOE_G32>(p, s);
+    case 16: return launch_bm<MOE_G16>(p, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -35,6 +35,8 @@ int check_device() {
   return st == 1 ? MOE_OK : MOE_ERR_DEVICE;
 }
 
+constexpr int64_t kMaxBufferBytes = (int64_t)1 << 31;
+
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
 bool valid_bm(int bm) { return bm == 16 || bm == 32 || bm == 64 || bm == 128; }
@@ -78,7 +80,13 @@ int validate_layer(const moe_layer_params* p) {
   if (p->activation != MOE_ACT_SWIGLU && p->activation != MOE_ACT_RELU2) return MOE_ERR_SHAPE;
   if (p->n_shared != 0 && p->n_shared != 1) return MOE_ERR_SHAPE;
   if ((int64_t)p->T * p->top_k > (1 << 28)) return MOE_ERR_SHAPE;
-  if ((int64_t)p->T * p->H > ((int64_t)1 << 40)) return MOE_ERR_SHAPE;
+  {  // byte offsets inside x, act and one expert's weights are 32-bit
+    const int64_t cap = MOE_ALIGN_CAPACITY(p->T, p->top_k, p->E, p->block_m);
+    const int64_t M1 = p->activation == MOE_ACT_SWIGLU ? 2 * (int64_t)p->I : p->I;
+    if ((int64_t)p->T * p->H * 2 >= kMaxBufferBytes || cap * p->I * 2 >= kMaxBufferBytes ||
+        M1 * p->H * 2 >= kMaxBufferBytes || (int64_t)p->H * p->I * 2 >= kMaxBufferBytes)
+      return MOE_ERR_UNSUPPORTED;
+  }
   return MOE_OK;
 }
 
@@ -193,6 +201,11 @@ int moe_grouped_gemm(const moe_gemm_args* args, void* workspace, size_t* workspa
   if (g.num_valid < 0 || g.a_row_div < 0) return MOE_ERR_SHAPE;
   if (g.a_row_div > 0 && g.num_valid % g.a_row_div != 0) return MOE_ERR_SHAPE;
   if (g.c_is_fp32 != 0 && g.c_is_fp32 != 1) return MOE_ERR_SHAPE;
+  {  // byte offsets inside one A matrix and one expert's W are 32-bit
+    const int64_t a_rows = g.a_row_div > 0 ? g.num_valid / g.a_row_div : g.capacity;
+    if (a_rows * g.K * 2 >= kMaxBufferBytes || (int64_t)g.N * g.K * 2 >= kMaxBufferBytes)
+      return MOE_ERR_UNSUPPORTED;
+  }
   if (workspace_bytes) *workspace_bytes = 0;   // this call needs no workspace
   if (g.capacity == 0) return MOE_OK;
   if (!g.a || !g.w || !g.c || !g.sorted_token_ids || !g.expert_ids || !g.num_tokens_post_padded)
@@ -220,6 +233,7 @@ int moe_grouped_gemm(const moe_gemm_args* args, void* workspace, size_t* workspa
   p.c_fp32 = g.c_is_fp32;
   p.c_row_offset = 0;
   p.ldc = g.epilogue == MOE_EPI_SWIGLU ? g.N / 2 : g.N;
+  p.a_rows = g.a_row_div > 0 ? g.num_valid / g.a_row_div : g.capacity;
   return hip_status(moe::launch_grouped_gemm(p, g.block_m, (hipStream_t)stream));
 }
 
@@ -338,6 +352,7 @@ int moe_fused_forward(const moe_layer_params* p, const void* x, const float* rou
   g1.C = L.act;
   g1.c_fp32 = 0;
   g1.ldc = I;
+  g1.a_rows = T;
   e = moe::launch_grouped_gemm(g1, bm, s);
   if (e != hipSuccess) return hip_status(e);
   if (p->n_shared) {
@@ -374,6 +389,7 @@ int moe_fused_forward(const moe_layer_params* p, const void* x, const float* rou
   g2.c_fp32 = 1;
   g2.c_row_offset = 0;
   g2.ldc = H;
+  g2.a_rows = (int)cap;
   e = moe::launch_grouped_gemm(g2, bm, s);
   if (e != hipSuccess) return hip_status(e);
   if (p->n_shared) {
@@ -387,6 +403,7 @@ int moe_fused_forward(const moe_layer_params* p, const void* x, const float* rou
     gs.M = T;
     gs.topk_w = nullptr;
     gs.c_row_offset = n;
+    gs.a_rows = T;
     e = moe::launch_grouped_gemm(gs, bm, s);
     if (e != hipSuccess) return hip_status(e);
   }

@@ -58,6 +58,8 @@ struct GemmParams {
   int c_fp32;
   int64_t c_row_offset;     // weighted scatter: added to the destination row
   int ldc;                  // output row stride in elements
+  int a_rows;               // rows of A (bounds of its buffer descriptor)
+  int mblocks, ntiles_n;    // tile grid (set by the launcher)
 };
 
 // ---------------------------------------------------------------- decode GEMVs
