@@ -26,6 +26,8 @@
 // v_mfma_f32_16x16x32_bf16 for BLOCK_M = 16.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -109,8 +111,9 @@ __device__ __forceinline__ int xcd_tile(int L, int n) {
 // kt + NS are issued while step kt is computed), MINW waves per SIMD.
 // SW: the tile's first BNW/2 weight rows are gate rows n0.., the rest the up
 // rows I+n0.. of the same act columns, and the epilogue is SwiGLU.
-template <int BM, int BNW, int WAVES_M, int WAVES_N, bool SW, int BK, int NS, int MINW>
-__global__ void __launch_bounds__(256, MINW) grouped_gemm_kernel(GemmParams p) {
+template <int BM, int BNW, int WAVES_M, int WAVES_N, bool SW, int BK, int NS, int MINW, bool DMA>
+__global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) grouped_gemm_kernel(GemmParams p) {
+  constexpr int NT = 64 * WAVES_M * WAVES_N;   // threads of the workgroup
   constexpr int CPR = BK / 8;
   constexpr int WM = BM / WAVES_M;
   constexpr int MT = WM >= 32 ? 32 : 16;
@@ -119,20 +122,25 @@ __global__ void __launch_bounds__(256, MINW) grouped_gemm_kernel(GemmParams p) {
   constexpr int WNW = BNW / WAVES_N;
   constexpr int FM = WM / MT;
   constexpr int FN = WNW / MT;
-  constexpr int XL = (BM * CPR + 255) / 256;
-  constexpr int WL = BNW * CPR / 256;
-  static_assert(WAVES_M * WAVES_N == 4, "4 waves");
+  constexpr int XL = (BM * CPR + NT - 1) / NT;
+  constexpr int WL = BNW * CPR / NT;
+  static_assert(WAVES_M * WAVES_N == 4 || WAVES_M * WAVES_N == 8, "4 or 8 waves");
   static_assert(!SW || FN % 2 == 0, "SwiGLU pairs gate and up subtiles");
-  static_assert(BNW * CPR % 256 == 0, "weight tile load");
+  static_assert(BNW * CPR % NT == 0, "weight tile load");
   static_assert(KSTEPS >= 1, "K step");
 
-  constexpr int NBUF = 3;
+  // LDS stages: three for the register-staged path; NS for the direct path
+  // (loads run NS - 1 K steps ahead)
+  constexpr int NBUF = DMA ? NS : 3;
+  static_assert(!DMA || NS >= 3, "direct-to-LDS pipeline needs three or more stages");
   __shared__ u32x4 sX[NBUF][BM * CPR];
   __shared__ u32x4 sW[NBUF][BNW * CPR];
+  auto bufx = [&](int b) { return sX[b]; };
+  auto bufw = [&](int b) { return sW[b]; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
   const int wn = wave % WAVES_N;
   const int wm = wave / WAVES_N;
 
@@ -163,7 +171,7 @@ __global__ void __launch_bounds__(256, MINW) grouped_gemm_kernel(GemmParams p) {
   int xoff[XL], xsa[XL], xch[XL];
 #pragma unroll
   for (int q = 0; q < XL; ++q) {
-    const int idx = tid + 256 * q;
+    const int idx = tid + NT * q;
     const int row = idx / CPR;
     xch[q] = idx % CPR;
     xsa[q] = swz<CPR>(row, xch[q]);
@@ -183,7 +191,7 @@ __global__ void __launch_bounds__(256, MINW) grouped_gemm_kernel(GemmParams p) {
   int woff[WL], wsa[WL], wch[WL];
 #pragma unroll
   for (int q = 0; q < WL; ++q) {
-    const int idx = tid + 256 * q;
+    const int idx = tid + NT * q;
     const int r = idx / CPR;
     wch[q] = idx % CPR;
     wsa[q] = swz<CPR>(r, wch[q]);
@@ -198,6 +206,48 @@ __global__ void __launch_bounds__(256, MINW) grouped_gemm_kernel(GemmParams p) {
       ok = g < p.N;
     }
     woff[q] = ok ? g * p.K * 2 + wch[q] * 16 : kNoRow;
+  }
+
+  // ---- direct-to-LDS: lane l of a wave load fills LDS unit (base + l); the
+  // unit at (row r, position pos) holds global chunk pos ^ mask(r), so the
+  // source offsets carry the swizzle and each row's lanes still read one line
+  int xdo[XL], wdo[WL];
+  if (DMA) {
+#pragma unroll
+    for (int q = 0; q < XL; ++q) {
+      const int u = tid + NT * q;
+      const int r = u / CPR;
+      const int c = (u % CPR) ^ ((r / (16 / CPR)) % CPR);
+      xdo[q] = kNoRow;
+      if (u < BM * CPR) {
+        const int i = m0 + r;
+        int arow = -1;
+        if (p.sorted_ids) {
+          const int sid = p.sorted_ids[i];
+          if (sid >= 0 && sid < p.num_valid) arow = p.a_row_div ? sid / p.a_row_div : i;
+        } else if (i < p.M) {
+          arow = i;
+        }
+        if (arow >= 0) xdo[q] = arow * p.K * 2 + c * 16;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < WL; ++q) {
+      const int u = tid + NT * q;
+      const int r = u / CPR;
+      const int c = (u % CPR) ^ ((r / (16 / CPR)) % CPR);
+      int g;
+      bool ok;
+      if (SW) {
+        const int cc = r < BNW / 2 ? n0 + r : n0 + r - BNW / 2;
+        ok = cc < p.I;
+        g = r < BNW / 2 ? cc : p.I + cc;
+      } else {
+        g = n0 + r;
+        ok = g < p.N;
+      }
+      wdo[q] = ok ? g * p.K * 2 + c * 16 : kNoRow;
+    }
   }
 
   // ---- LDS read addresses: every operand row a lane reads is row(lane) plus
@@ -249,10 +299,66 @@ __global__ void __launch_bounds__(256, MINW) grouped_gemm_kernel(GemmParams p) {
       wr[q] = __builtin_amdgcn_raw_buffer_load_b128(wr_rs, off, 0, 0);
     }
   };
+  // direct-to-LDS loads of K step kt into LDS buffer b.  Issued from inline
+  // asm (buffer_load_dwordx4 ... lds; M0 holds the wave's LDS destination and
+  // is restored) so that the compiler, which cannot tell the in-flight
+  // transfers from the LDS reads of other buffers, does not wait for all of
+  // them before every read; completion is awaited explicitly (vmcnt) before
+  // the barrier that publishes a step.  The asm writes no register.
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  auto rsrc4 = [](const void* base, int64_t bytes) {
+    const uint64_t a = (uint64_t)base;
+    return i32x4{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xffffu), (int)bytes, 0x00020000};
+  };
+  const i32x4 xr4 = rsrc4(p.A, (int64_t)p.a_rows * p.K * 2);
+  const i32x4 wr4 = rsrc4(We, (int64_t)p.N * p.K * 2);
+  auto dma1 = [](const i32x4& rs, const void* lds, int voff, int soff) {
+    const unsigned la = (unsigned)(uintptr_t)(const __attribute__((address_space(3))) void*)lds;
+    int m0save;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(m0save)
+        : "s"(la), "v"(voff), "s"(rs), "s"(soff)
+        : "memory");
+  };
+  // waves whose X part of the tile is empty (BM * CPR < 256) issue no X load
+  const bool x_wave = 64 * wave < BM * CPR;
+  auto dma = [&](int kt, int b) {
+    const int k0 = kt * BK;
+    const bool tail = (kt + 1) * BK > p.K;
+#pragma unroll
+    for (int q = 0; q < XL; ++q) {
+      if (NT * q + 64 * wave >= BM * CPR) continue;   // wave-uniform
+      const int u = tid + NT * q;
+      int off = xdo[q], soff = k0 * 2;
+      if (tail) {
+        const int c = (u % CPR) ^ ((u / CPR / (16 / CPR)) % CPR);
+        off = (k0 + c * 8 < p.K && off != kNoRow) ? off + k0 * 2 : kNoRow;
+        soff = 0;
+      }
+      dma1(xr4, sX[b] + NT * q + 64 * wave, off, soff);
+    }
+#pragma unroll
+    for (int q = 0; q < WL; ++q) {
+      const int u = tid + NT * q;
+      int off = wdo[q], soff = k0 * 2;
+      if (tail) {
+        const int c = (u % CPR) ^ ((u / CPR / (16 / CPR)) % CPR);
+        off = (k0 + c * 8 < p.K && off != kNoRow) ? off + k0 * 2 : kNoRow;
+        soff = 0;
+      }
+      dma1(wr4, sW[b] + NT * q + 64 * wave, off, soff);
+    }
+  };
+  // DMA instructions one thread issues per K step
+  constexpr int XLW = (BM * CPR) / NT > 0 ? (BM * CPR) / NT : 1;
   auto sstore = [&](u32x4* sx, u32x4* sw) {
 #pragma unroll
     for (int q = 0; q < XL; ++q)
-      if (tid + 256 * q < BM * CPR) sx[xsa[q]] = xr[q];
+      if (tid + NT * q < BM * CPR) sx[xsa[q]] = xr[q];
 #pragma unroll
     for (int q = 0; q < WL; ++q) sw[wsa[q]] = wr[q];
   };
@@ -284,28 +390,107 @@ __global__ void __launch_bounds__(256, MINW) grouped_gemm_kernel(GemmParams p) {
   auto load_step = [&](int kt) {
     if (ktail && kt == nk - 1) gload_tail(kt); else gload(kt);
   };
+  if constexpr (DMA) {
+    // vmcnt(n) with the other counters left alone; n = loads one thread
+    // issues per K step (a compile-time count per kind of wave)
+    constexpr int NXW = XL + WL;
+    constexpr int NW = WL + (XL > 1 ? XL - 1 : 0);
+    static_assert(BM * CPR % NT == 0 || XL == 1, "X loads per wave are all-or-one");
+    constexpr int D = NBUF - 1;   // prefetch distance in K steps
+    static_assert((D - 1) * NXW <= 63, "vmcnt range");
+    // wait until this thread's loads of the oldest pending step have landed,
+    // `later` steps issued after it may stay in flight
+    auto wait_steps = [&](int later) {
+#define MOE_VMW(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+      const int n = later * (x_wave ? NXW : NW);
+      switch (n) {  // s_waitcnt takes an immediate
+#define MOE_VMW_CASE(i) case i: MOE_VMW(i); break;
+        MOE_VMW_CASE(0) MOE_VMW_CASE(1) MOE_VMW_CASE(2) MOE_VMW_CASE(3) MOE_VMW_CASE(4)
+        MOE_VMW_CASE(5) MOE_VMW_CASE(6) MOE_VMW_CASE(7) MOE_VMW_CASE(8) MOE_VMW_CASE(9)
+        MOE_VMW_CASE(10) MOE_VMW_CASE(11) MOE_VMW_CASE(12) MOE_VMW_CASE(13) MOE_VMW_CASE(14)
+        MOE_VMW_CASE(15) MOE_VMW_CASE(16) MOE_VMW_CASE(18) MOE_VMW_CASE(20) MOE_VMW_CASE(21)
+        MOE_VMW_CASE(24) MOE_VMW_CASE(25) MOE_VMW_CASE(27) MOE_VMW_CASE(28) MOE_VMW_CASE(30)
+        MOE_VMW_CASE(32) MOE_VMW_CASE(35) MOE_VMW_CASE(36) MOE_VMW_CASE(40) MOE_VMW_CASE(42)
+        MOE_VMW_CASE(45) MOE_VMW_CASE(48) MOE_VMW_CASE(49) MOE_VMW_CASE(50) MOE_VMW_CASE(54)
+        MOE_VMW_CASE(56) MOE_VMW_CASE(60) MOE_VMW_CASE(63)
+        default: MOE_VMW(0); break;   // a count not listed: wait for everything (safe)
+#undef MOE_VMW_CASE
+#undef MOE_VMW
+      }
+    };
+    (void)XLW;
+    for (int st = 0; st < D; ++st)
+      if (st < nk) dma(st, st);
+    wait_steps(min(D, nk) - 1);
+    __builtin_amdgcn_s_barrier();
+    int b0 = 0;
+    for (int kt = 0; kt < nk; ++kt) {
+      const int bd = b0 == 0 ? NBUF - 1 : b0 - 1;   // (kt + D) % NBUF
+      if (kt + D < nk) dma(kt + D, bd);
+      const u32x4* const rx = sX[b0];
+      const u32x4* const rw = sW[b0];
+      Ops sa, sb;
+      read_ops(rx, rw, 0, sa);
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; kk += 2) {
+        if (kk + 1 < KSTEPS) read_ops(rx, rw, kk + 1, sb);
+        mfmas(sa);
+        if (kk + 2 < KSTEPS) read_ops(rx, rw, kk + 2, sa);
+        if (kk + 1 < KSTEPS) mfmas(sb);
+      }
+      if (kt + 1 < nk) {
+        // this thread's part of step kt + 1 has landed; steps kt + 2 .. kt + D
+        // (those issued) may still be in flight
+        wait_steps(min(kt + D, nk - 1) - (kt + 1));
+        __builtin_amdgcn_s_barrier();
+      }
+      b0 = b0 == NBUF - 1 ? 0 : b0 + 1;
+    }
+  } else {
   load_step(0);
-  sstore(sX[0], sW[0]);
+  sstore(bufx(0), bufw(0));
   if (nk > 1) load_step(1);
   __syncthreads();
-  Ops cur, nxt;
-  read_ops(sX[0], sW[0], 0, cur);
+  // two operand register sets used in turn: while the MFMAs of one substep
+  // read set A, the LDS reads of the next substep fill set B (no copies)
+  static_assert(KSTEPS % 2 == 0 || KSTEPS == 1, "substeps pair up");
+  Ops sa, sb;
+  read_ops(bufx(0), bufw(0), 0, sa);
   int b0 = 0;   // buffer of step kt
   for (int kt = 0; kt < nk; ++kt) {
     const int b1 = b0 == NBUF - 1 ? 0 : b0 + 1;
-    if (kt + 1 < nk) sstore(sX[b1], sW[b1]);
+    if (kt + 1 < nk) sstore(bufx(b1), bufw(b1));
     if (kt + 2 < nk) load_step(kt + 2);
     __syncthreads();
+    const bool more = kt + 1 < nk;
+    if constexpr (KSTEPS == 1) {
+      // one substep per K step: alternate the sets across K steps
+      if (more) read_ops(bufx(b1), bufw(b1), 0, sb);
+      mfmas(sa);
+      ++kt;
+      b0 = b1;
+      if (kt >= nk) break;
+      const int b2 = b0 == NBUF - 1 ? 0 : b0 + 1;
+      if (kt + 1 < nk) sstore(bufx(b2), bufw(b2));
+      if (kt + 2 < nk) load_step(kt + 2);
+      __syncthreads();
+      if (kt + 1 < nk) read_ops(bufx(b2), bufw(b2), 0, sa);
+      mfmas(sb);
+      b0 = b2;
+    } else {
 #pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk) {
-      if (kk + 1 < KSTEPS)
-        read_ops(sX[b0], sW[b0], kk + 1, nxt);
-      else if (kt + 1 < nk)
-        read_ops(sX[b1], sW[b1], 0, nxt);
-      mfmas(cur);
-      cur = nxt;
+      for (int kk = 0; kk < KSTEPS; kk += 2) {
+        read_ops(bufx(b0), bufw(b0), kk + 1, sb);
+        mfmas(sa);
+        if (kk + 2 < KSTEPS)
+          read_ops(bufx(b0), bufw(b0), kk + 2, sa);
+        else if (more)
+          read_ops(bufx(b1), bufw(b1), 0, sa);
+        mfmas(sb);
+      }
+      b0 = b1;
     }
-    b0 = b1;
+  }
   }
 
   // ---- epilogue
@@ -369,7 +554,7 @@ __global__ void __launch_bounds__(256, MINW) grouped_gemm_kernel(GemmParams p) {
   }
 }
 
-template <int BM, int BNW, int WAVES_M, int WAVES_N, int BK, int NS, int MINW>
+template <int BM, int BNW, int WAVES_M, int WAVES_N, int BK, int NS, int MINW, bool DMA>
 hipError_t launch_bm(GemmParams p, hipStream_t s) {
   const bool sw = p.epi == 1;
   const int ncols = sw ? p.I : p.N;
@@ -379,11 +564,11 @@ hipError_t launch_bm(GemmParams p, hipStream_t s) {
   const int64_t nwg = (int64_t)p.mblocks * p.ntiles_n;
   if (nwg == 0) return hipSuccess;
   if (sw)
-    hipLaunchKernelGGL((grouped_gemm_kernel<BM, BNW, WAVES_M, WAVES_N, true, BK, NS, MINW>),
-                       dim3((unsigned)nwg), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((grouped_gemm_kernel<BM, BNW, WAVES_M, WAVES_N, true, BK, NS, MINW, DMA>),
+                       dim3((unsigned)nwg), dim3(64 * WAVES_M * WAVES_N), 0, s, p);
   else
-    hipLaunchKernelGGL((grouped_gemm_kernel<BM, BNW, WAVES_M, WAVES_N, false, BK, NS, MINW>),
-                       dim3((unsigned)nwg), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((grouped_gemm_kernel<BM, BNW, WAVES_M, WAVES_N, false, BK, NS, MINW, DMA>),
+                       dim3((unsigned)nwg), dim3(64 * WAVES_M * WAVES_N), 0, s, p);
   return hipGetLastError();
 }
 
@@ -391,16 +576,16 @@ hipError_t launch_bm(GemmParams p, hipStream_t s) {
 
 // Tile configurations per BLOCK_M (compile-time knobs, defaults tuned on MI355X).
 #ifndef MOE_G128
-#define MOE_G128 128, 256, 2, 2, 32, 1, 2
+#define MOE_G128 128, 256, 2, 2, 32, 3, 2, true
 #endif
 #ifndef MOE_G64
-#define MOE_G64 64, 256, 1, 4, 64, 2, 1
+#define MOE_G64 64, 256, 1, 4, 32, 3, 2, true
 #endif
 #ifndef MOE_G32
-#define MOE_G32 32, 256, 1, 4, 64, 2, 1
+#define MOE_G32 32, 256, 1, 4, 32, 3, 2, true
 #endif
 #ifndef MOE_G16
-#define MOE_G16 16, 128, 1, 4, 64, 2, 2
+#define MOE_G16 16, 128, 1, 4, 64, 3, 2, true
 #endif
 
 hipError_t launch_grouped_gemm(const GemmParams& p, int block_m, hipStream_t s) {
