@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--cpu-tokens", type=int, default=4096,
                     help="tokens of the workload the CPU oracle runs on")
     ap.add_argument("--extra", default="", help="comma list of more configs to time (report only)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a device-to-device copy of known size (scales the HBM "
+                         "byte counters of a profiler pass) and exit")
     return ap.parse_args()
 
 
@@ -181,6 +184,22 @@ def cpu_baseline(cfg, inp, ntok, W, O, min_seconds=10.0):
                       f"({dt:.2f} s, fp64 numpy per-expert loop incl. weight widening)"}
 
 
+def copy_calibration(torch, nbytes=1 << 30, reps=4):
+    """Copies of ``nbytes`` (read nbytes, write nbytes per launch), for turning
+    the FETCH_SIZE / WRITE_SIZE counters of the same profiler into bytes: a
+    device-to-device ``copy_`` and an elementwise negation (a streaming kernel
+    of the same traffic that is certain to be a shader dispatch)."""
+    a = torch.full((nbytes // 4,), 1.0, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    for _ in range(reps):
+        torch.neg(a, out=b)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read": nbytes, "bytes_written": nbytes,
+                                           "launches": reps}}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -196,6 +215,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
     moe.lib()
     cfg = W.CONFIGS[args.config]
     inp = W.make_inputs(cfg)
@@ -223,7 +245,7 @@ def main():
                    "routed_only_TFLOPS": round(cfg.flops(routed_only=True) / (ms * 1e-3) / 1e12, 2),
                    "mfma_frac_of_layer": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                    "wall_s_timed": round(wall, 3)},
-        "roofline": {"bound": "mfma", "kernel": "grouped_gemm_kernel<128,256,2,2,SwiGLU>",
+        "roofline": {"bound": "mfma", "kernel": "grouped_gemm_kernel<128, 256, 2, 2, true, 32, 3, 2, true> (routed W13 + SwiGLU)",
                      "achieved": round(gemm_tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tf / MFMA_BF16_PEAK_TFLOPS, 4),
                      "traffic": None, "avg_launch_us": round(gemm_ms * 1e3, 2),

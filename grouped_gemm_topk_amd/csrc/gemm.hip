@@ -99,11 +99,34 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
   return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
 }
 
+#ifndef MOE_GM
+#define MOE_GM 8   // m-blocks per tile chunk
+#endif
+
 __device__ __forceinline__ int xcd_tile(int L, int n) {
   // workgroups are handed to the 8 XCDs round-robin by linear id: give XCD x
   // the contiguous tile range [start(x), start(x + 1))
   const int q = n >> 3, r = n & 7, x = L & 7;
   return x * q + (x < r ? x : r) + (L >> 3);
+}
+
+// [rs, re): the maximal run of m-blocks around mb0 (below vb) that hold the
+// same expert id; wave-uniform, 64 ids per probe.
+__device__ __forceinline__ void expert_run(const int* __restrict__ expert_ids, int mb0, int vb,
+                                           int lane, int& rs, int& re) {
+  const int e0 = expert_ids[mb0];
+  for (int base = mb0 - 1;; base -= 64) {
+    const int idx = base - lane;
+    const bool stop = idx < 0 || expert_ids[idx < 0 ? 0 : idx] != e0;
+    const uint64_t b = __ballot(stop);
+    if (b) { rs = base - (int)__builtin_ctzll(b) + 1; break; }
+  }
+  for (int base = mb0 + 1;; base += 64) {
+    const int idx = base + lane;
+    const bool stop = idx >= vb || expert_ids[idx >= vb ? mb0 : idx] != e0;
+    const uint64_t b = __ballot(stop);
+    if (b) { re = base + (int)__builtin_ctzll(b); break; }
+  }
 }
 
 // BM token rows x BNW weight rows per workgroup tile, WAVES_M x WAVES_N waves,
@@ -144,19 +167,26 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) grouped_gemm_ker
   const int wn = wave % WAVES_N;
   const int wm = wave / WAVES_N;
 
-  // ---- tile of this workgroup: XCD-contiguous, groups of GM m-blocks per n-tile
+  // ---- tile of this workgroup: XCD-contiguous; the tiles of each expert's
+  // run of m-blocks are consecutive, in chunks of GM m-blocks with the n-tile
+  // outer, so that neighbouring workgroups share weight tiles and token rows
   const int ntn = p.ntiles_n, nmb = p.mblocks;
   const int t = xcd_tile(blockIdx.x, ntn * nmb);
-  constexpr int GM = 8;
-  const int grp = t / (GM * ntn);
-  const int gsz = min(GM, nmb - grp * GM);
-  const int j = t - grp * GM * ntn;
-  const int mb = grp * GM + j % gsz;
+  const int total_rows = p.ntpp ? *p.ntpp : p.M;
+  const int vb = min(nmb, (total_rows + BM - 1) / BM);   // m-blocks holding rows
+  const int mb0 = t / ntn;
+  if (mb0 >= vb) return;
+  int rs = 0, re = vb;
+  if (p.expert_ids) expert_run(p.expert_ids, mb0, vb, lane, rs, re);
+  constexpr int GM = MOE_GM;
+  const int jr = t - rs * ntn;
+  const int grp = jr / (GM * ntn);
+  const int gsz = min(GM, re - rs - grp * GM);
+  const int j = jr - grp * GM * ntn;
+  const int mb = rs + grp * GM + j % gsz;
   const int nt = j / gsz;
 
   const int m0 = mb * BM;
-  const int total_rows = p.ntpp ? *p.ntpp : p.M;
-  if (m0 >= total_rows) return;
   const int e = p.expert_ids ? p.expert_ids[mb] : 0;
   if (e < 0 || e >= p.E) return;
   const uint16_t* We = p.W + (int64_t)e * p.N * p.K;
