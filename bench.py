@@ -31,6 +31,19 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 MALL_BYTES = 256 << 20           # Infinity Cache
 
+# HBM-side bytes per launch of the dominant kernel (routed SwiGLU grouped GEMM
+# of the dsv3 layer) from two rocprofv3 counter passes: FETCH_SIZE x 2.0 and
+# WRITE_SIZE x 1.0, the factors that turn the same counters into the known
+# bytes of a 1 GiB device copy.  Valid only for the kernel source with this
+# digest; any other source reports traffic null until it is measured again.
+DOMINANT_TRAFFIC = {
+    "src": "grouped_gemm_topk_amd/csrc/gemm.hip",
+    "sha256": "af5f447447b1db1b8b78e9256d2b08bf3b7a3e1bc5d451dbf8099a842f11173b",
+    "config": "dsv3",
+    "fetch_bytes": 1310411366,
+    "write_bytes": 94166016,
+}
+
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
@@ -184,6 +197,21 @@ def cpu_baseline(cfg, inp, ntok, W, O, min_seconds=10.0):
                       f"({dt:.2f} s, fp64 numpy per-expert loop incl. weight widening)"}
 
 
+def dominant_traffic(cfg_name):
+    """Counter-derived bytes per launch, or None when the kernel source has
+    changed since the counters were taken (or for another workload)."""
+    import hashlib
+    t = DOMINANT_TRAFFIC
+    try:
+        with open(os.path.join(ROOT, t["src"]), "rb") as f:
+            digest = hashlib.sha256(f.read()).hexdigest()
+    except OSError:
+        return None
+    if digest != t["sha256"] or cfg_name != t["config"]:
+        return None
+    return t["fetch_bytes"] + t["write_bytes"]
+
+
 def copy_calibration(torch, nbytes=1 << 30, reps=4):
     """Copies of ``nbytes`` (read nbytes, write nbytes per launch), for turning
     the FETCH_SIZE / WRITE_SIZE counters of the same profiler into bytes: a
@@ -232,6 +260,9 @@ def main():
     gemm_ms = time_dominant_gemm(cfg, layer, args.steps, args.warmup, torch, moe)
     gemm_flops = 2.0 * cfg.T * cfg.top_k * cfg.H * 2 * cfg.I
     gemm_tf = gemm_flops / (gemm_ms * 1e-3) / 1e12
+    # algorithmic bytes: every routed expert's W13 once, each token row once,
+    # the activation rows of every (token, slot) pair written once
+    gemm_alg_bytes = (cfg.E * 2 * cfg.I * cfg.H + cfg.T * cfg.H + cfg.T * cfg.top_k * cfg.I) * 2
     line = {
         "metric": "fused-MoE layer TFLOPS at T=4096 + decode us/layer (T=1..8) vs roofline",
         "value": round(tflops, 2), "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps,
@@ -248,7 +279,10 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "grouped_gemm_kernel<128, 256, 2, 2, true, 32, 3, 2, true> (routed W13 + SwiGLU)",
                      "achieved": round(gemm_tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tf / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": None, "avg_launch_us": round(gemm_ms * 1e3, 2),
+                     "traffic": dominant_traffic(cfg.name),
+                     "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled)",
+                     "alg_bytes_per_launch": gemm_alg_bytes,
+                     "avg_launch_us": round(gemm_ms * 1e3, 2),
                      "alg_flops_per_launch": gemm_flops},
     }
     if not args.no_decode:
