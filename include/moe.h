@@ -8,7 +8,8 @@
  * then a tiled grouped GEMM that reaches its token rows through
  * `sorted_token_ids` and its weight matrix through `expert_ids`, skipping
  * blocks at or beyond `num_tokens_post_padded`.  The expert MLP is SwiGLU
- * (`act_fn(gate) * up`, the axolotl DeepSeek-V3 MoE forward) or squared ReLU
+ * (silu of the gate rows times the up rows, as in the axolotl DeepSeek-V3 MoE
+ * forward) or squared ReLU
  * (fc1 -> relu^2 -> fc2, mlxcel PR #280).
  *
  * Conventions shared by every entry point

@@ -5,8 +5,8 @@ baseline leg of the benchmark may import this module; the library's product
 path never does.  It shares no code with the HIP implementation.
 
 The oracle is deliberately plain and slow: a per-expert loop, the structure the
-pages use as their reference ("sequential per-expert torch.matmul with top-k
-selection", Fused Moe Kernel skill card, *Verification*; the per-group matmul
+pages use as their reference (the skill card's *Verification* checks against
+one matmul per expert after top-k selection; the per-group matmul
 loop ``pytorch_reference`` in the axolotl branch's ``cg_forward.py``; the
 per-expert Python loop of the Gemma-4 training note).  Floating point is
 carried in float64; bf16 inputs are widened exactly.
@@ -65,8 +65,8 @@ def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
 def select_topk(logits: np.ndarray, k: int, allowed: Optional[np.ndarray] = None) -> np.ndarray:
     """Top-k expert ids per token, as k rounds of arg-max.
 
-    Fused Moe Kernel skill card, *Token-Expert Routing* step 1 ("select k
-    experts per token").  Each round picks the largest remaining logit; among
+    Fused Moe Kernel skill card, *Token-Expert Routing* step 1 (each token
+    keeps k experts).  Each round picks the largest remaining logit; among
     equal logits ``np.argmax`` returns the first, i.e. the lower expert index.
     ``allowed`` (bool [T,E]) restricts the candidates (grouped routing).
     Returns int32 [T,k] in selection order.
@@ -212,13 +212,13 @@ def align(topk_ids: np.ndarray, E: int, block_m: int) -> Dict[str, np.ndarray]:
 # 3. expert MLP and combine
 # ----------------------------------------------------------------------------
 def silu(z: np.ndarray) -> np.ndarray:
-    """z * sigmoid(z) (``hidden_act="silu"`` of the DeepSeek-V3 config)."""
+    """z * sigmoid(z), the SiLU activation of the DeepSeek-V3 config."""
     return z / (1.0 + np.exp(-z))
 
 
 def activation(h: np.ndarray, act: int, I: int) -> np.ndarray:
-    """SwiGLU ``act_fn(gate) * up`` with gate = h[:, :I], up = h[:, I:] (the
-    axolotl MoE forward), or squared ReLU max(h, 0)^2 (mlxcel fc1 -> relu^2)."""
+    """SwiGLU: silu of the gate half h[:, :I] times the up half h[:, I:] (the
+    order of the axolotl MoE forward), or squared ReLU max(h, 0)^2 (mlxcel fc1 -> relu^2)."""
     if act == ACT_SWIGLU:
         return silu(h[:, :I]) * h[:, I:]
     if act == ACT_RELU2:
