@@ -6,22 +6,28 @@
 // sorted_token_ids (token = id / top_k, *Common Pitfalls* 1), whose weight
 // matrix is chosen per M-block by expert_ids (weights stacked [E, N, K],
 // *Common Pitfalls* 3), and whose blocks at or beyond num_tokens_post_padded
-// exit at once.  Epilogues: SwiGLU act_fn(gate) * up (axolotl DeepSeek-V3 MoE
+// exit at once.  Epilogues: SwiGLU, silu(gate) times up (axolotl DeepSeek-V3 MoE
 // forward), squared ReLU (mlxcel fc1 -> relu^2), plain store, and the routed
 // weight times the row scattered to its slot (*Common Pitfalls* 4).
 //
-// gfx950 mapping.  One workgroup = 4 wave64s computes a BM x BNW tile of
-// C^T = W_e . X^T: the weight rows play the MFMA "A" role and the gathered
+// gfx950 mapping.  One workgroup of 4 or 8 wave64s computes a BM x BNW tile
+// of C^T = W_e . X^T: the weight rows play the MFMA "A" role and the gathered
 // token rows the "B" role, so each lane ends up owning 4 consecutive output
 // features of one token row and stores them as one 8- or 16-byte write.
-// Operands are staged global -> registers -> LDS: buffer loads run NS K steps
-// ahead of the MFMAs in register stages, LDS is double buffered with one
-// barrier per K step, and the LDS chunk order is XOR-swizzled so MFMA operand
-// reads and the stores are free of bank conflicts.  Workgroups are mapped to
-// tiles XCD by XCD (each XCD gets a contiguous tile range) and, inside a
-// range, in groups of 8 M-blocks per N-tile so that a weight tile is reused
-// from that XCD's L2 (the L2 grouping / cache-aware scheduling of the skill
-// card's *Optimization Patterns*).
+// Operands go global -> LDS directly (buffer loads with the LDS destination
+// bit) through an NS-stage ring of LDS buffers, NS - 1 K steps ahead of the
+// MFMAs, with one barrier per K step.  A K step is 64 elements wide so each
+// row chunk is one full 128-byte line (64-byte chunks halve what the
+// load path delivers per CU).  Each thread's loads of a later step are spread
+// between the MFMAs of the current one instead of being issued as a burst,
+// which kept the address queue full and stalled the issuing waves.  The LDS
+// chunk order is XOR-swizzled so the MFMA operand reads are free of bank
+// conflicts.  Workgroups are mapped to tiles XCD by XCD (each XCD gets a
+// contiguous tile range) and, inside a range, the tiles of one expert's run
+// of M-blocks are consecutive, in chunks of 8 M-blocks per N-tile, so that a
+// weight tile and the token rows are reused from that XCD's L2 (the L2
+// grouping / cache-aware scheduling of the skill card's *Optimization
+// Patterns*).
 // v_mfma_f32_32x32x16_bf16 is used when a wave owns >= 32 token rows,
 // v_mfma_f32_16x16x32_bf16 for BLOCK_M = 16.
 #include <hip/hip_runtime.h>
@@ -130,8 +136,8 @@ __device__ __forceinline__ void expert_run(const int* __restrict__ expert_ids, i
 }
 
 // BM token rows x BNW weight rows per workgroup tile, WAVES_M x WAVES_N waves,
-// BK-wide K steps, NS register stages of global prefetch (loads for step
-// kt + NS are issued while step kt is computed), MINW waves per SIMD.
+// BK-wide K steps, NS LDS stages (direct path: loads for step kt + NS - 1 are
+// issued while step kt is computed), MINW workgroups per CU requested.
 // SW: the tile's first BNW/2 weight rows are gate rows n0.., the rest the up
 // rows I+n0.. of the same act columns, and the epilogue is SwiGLU.
 template <int BM, int BNW, int WAVES_M, int WAVES_N, bool SW, int BK, int NS, int MINW, bool DMA>
@@ -155,7 +161,7 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) grouped_gemm_ker
   // LDS stages: three for the register-staged path; NS for the direct path
   // (loads run NS - 1 K steps ahead)
   constexpr int NBUF = DMA ? NS : 3;
-  static_assert(!DMA || NS >= 3, "direct-to-LDS pipeline needs three or more stages");
+  static_assert(!DMA || NS >= 2, "direct-to-LDS pipeline needs two or more stages");
   __shared__ u32x4 sX[NBUF][BM * CPR];
   __shared__ u32x4 sW[NBUF][BNW * CPR];
   auto bufx = [&](int b) { return sX[b]; };
@@ -356,32 +362,33 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) grouped_gemm_ker
   };
   // waves whose X part of the tile is empty (BM * CPR < 256) issue no X load
   const bool x_wave = 64 * wave < BM * CPR;
-  auto dma = [&](int kt, int b) {
+  // load i (of XL + WL per thread) of K step kt into LDS buffer b: the first
+  // XL are token-row chunks, the rest weight-row chunks; the ragged last K
+  // step (tail) masks the 16-byte chunks beyond K
+  auto dma_one = [&](auto tail_c, int kt, int b, int i) {
+    constexpr bool tail = decltype(tail_c)::value;
     const int k0 = kt * BK;
-    const bool tail = (kt + 1) * BK > p.K;
-#pragma unroll
-    for (int q = 0; q < XL; ++q) {
-      if (NT * q + 64 * wave >= BM * CPR) continue;   // wave-uniform
-      const int u = tid + NT * q;
-      int off = xdo[q], soff = k0 * 2;
-      if (tail) {
-        const int c = (u % CPR) ^ ((u / CPR / (16 / CPR)) % CPR);
-        off = (k0 + c * 8 < p.K && off != kNoRow) ? off + k0 * 2 : kNoRow;
-        soff = 0;
-      }
-      dma1(xr4, sX[b] + NT * q + 64 * wave, off, soff);
+    const bool is_x = i < XL;
+    const int q = is_x ? i : i - XL;
+    if (is_x && NT * q + 64 * wave >= BM * CPR) return;   // wave-uniform
+    const int u = tid + NT * q;
+    int off = is_x ? xdo[is_x ? q : 0] : wdo[is_x ? 0 : q], soff = k0 * 2;
+    if constexpr (tail) {
+      const int c = (u % CPR) ^ ((u / CPR / (16 / CPR)) % CPR);
+      off = (k0 + c * 8 < p.K && off != kNoRow) ? off + k0 * 2 : kNoRow;
+      soff = 0;
     }
+    if (is_x) dma1(xr4, sX[b] + NT * q + 64 * wave, off, soff);
+    else dma1(wr4, sW[b] + NT * q + 64 * wave, off, soff);
+  };
+  // one whole K step of direct loads into LDS buffer b
+  auto dma_step = [&](auto tail_c, int kt, int b) {
 #pragma unroll
-    for (int q = 0; q < WL; ++q) {
-      const int u = tid + NT * q;
-      int off = wdo[q], soff = k0 * 2;
-      if (tail) {
-        const int c = (u % CPR) ^ ((u / CPR / (16 / CPR)) % CPR);
-        off = (k0 + c * 8 < p.K && off != kNoRow) ? off + k0 * 2 : kNoRow;
-        soff = 0;
-      }
-      dma1(wr4, sW[b] + NT * q + 64 * wave, off, soff);
-    }
+    for (int i = 0; i < XL + WL; ++i) dma_one(tail_c, kt, b, i);
+  };
+  auto dma = [&](int kt, int b) {
+    if ((kt + 1) * BK > p.K) dma_step(std::true_type{}, kt, b);
+    else dma_step(std::false_type{}, kt, b);
   };
   // DMA instructions one thread issues per K step
   constexpr int XLW = (BM * CPR) / NT > 0 ? (BM * CPR) / NT : 1;
@@ -408,13 +415,35 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) grouped_gemm_ker
 #pragma unroll
       for (int q = 0; q < FM; ++q) acc[f][q] = M::run(o.a[f], o.b[q], acc[f][q]);
   };
+  // the MFMAs of substep kk with this thread's loads of a later K step spread
+  // between them: load i follows MFMA i * TM / ND of the step, so the address
+  // queue drains while the matrix cores work
+  auto mfmas_spread = [&](const Ops& o, int kk, auto&& load_i) {
+    constexpr int TM = KSTEPS * FN * FM;
+    constexpr int ND = XL + WL;
+#pragma unroll
+    for (int f = 0; f < FN; ++f)
+#pragma unroll
+      for (int q = 0; q < FM; ++q) {
+        acc[f][q] = M::run(o.a[f], o.b[q], acc[f][q]);
+        const int m = (kk * FN + f) * FM + q;
+#pragma unroll
+        for (int i = 0; i < ND; ++i)
+          if (i * TM / ND == m) load_i(i);
+      }
+  };
 
-  // ---- pipeline over K steps with three LDS buffers and one barrier per step.
-  // Step kt: store step kt + 1 (loaded during step kt - 1) into buffer
-  // (kt + 1) % 3, request step kt + 2, barrier (step kt + 1 is now visible and
-  // every wave is done reading buffer (kt + 2) % 3), then the MFMAs of step kt
-  // with each k-substep's operands read one substep ahead; the first
-  // substep of step kt + 1 is read during the last MFMAs of step kt.
+  // ---- pipeline over K steps, one barrier per step.
+  // Direct path (NBUF = NS buffers, D = NS - 1): step kt computes from buffer
+  // kt % NBUF while its MFMAs interleave the loads of step kt + D into the
+  // buffer that step kt - 1 used (every wave is past the barrier that ended
+  // step kt - 1); then each thread waits for its own loads of step kt + 1 and
+  // the barrier makes them visible to all waves.
+  // Register path (three buffers): step kt stores step kt + 1 (loaded during
+  // step kt - 1) into buffer (kt + 1) % 3, requests step kt + 2, barrier, then
+  // the MFMAs of step kt with each k-substep's operands read one substep
+  // ahead; the first substep of step kt + 1 is read during the last MFMAs of
+  // step kt.
   const int nk = (p.K + BK - 1) / BK;
   const bool ktail = p.K % BK != 0;
   auto load_step = [&](int kt) {
@@ -428,35 +457,29 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) grouped_gemm_ker
     static_assert(BM * CPR % NT == 0 || XL == 1, "X loads per wave are all-or-one");
     constexpr int D = NBUF - 1;   // prefetch distance in K steps
     static_assert((D - 1) * NXW <= 63, "vmcnt range");
-    // wait until this thread's loads of the oldest pending step have landed,
-    // `later` steps issued after it may stay in flight
-    auto wait_steps = [&](int later) {
+    // wait until this thread's loads of the oldest pending step have landed;
+    // in steady state D - 1 later steps stay in flight (a compile-time count
+    // per kind of wave), near the end of K everything is waited for
 #define MOE_VMW(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
-      const int n = later * (x_wave ? NXW : NW);
-      switch (n) {  // s_waitcnt takes an immediate
-#define MOE_VMW_CASE(i) case i: MOE_VMW(i); break;
-        MOE_VMW_CASE(0) MOE_VMW_CASE(1) MOE_VMW_CASE(2) MOE_VMW_CASE(3) MOE_VMW_CASE(4)
-        MOE_VMW_CASE(5) MOE_VMW_CASE(6) MOE_VMW_CASE(7) MOE_VMW_CASE(8) MOE_VMW_CASE(9)
-        MOE_VMW_CASE(10) MOE_VMW_CASE(11) MOE_VMW_CASE(12) MOE_VMW_CASE(13) MOE_VMW_CASE(14)
-        MOE_VMW_CASE(15) MOE_VMW_CASE(16) MOE_VMW_CASE(18) MOE_VMW_CASE(20) MOE_VMW_CASE(21)
-        MOE_VMW_CASE(24) MOE_VMW_CASE(25) MOE_VMW_CASE(27) MOE_VMW_CASE(28) MOE_VMW_CASE(30)
-        MOE_VMW_CASE(32) MOE_VMW_CASE(35) MOE_VMW_CASE(36) MOE_VMW_CASE(40) MOE_VMW_CASE(42)
-        MOE_VMW_CASE(45) MOE_VMW_CASE(48) MOE_VMW_CASE(49) MOE_VMW_CASE(50) MOE_VMW_CASE(54)
-        MOE_VMW_CASE(56) MOE_VMW_CASE(60) MOE_VMW_CASE(63)
-        default: MOE_VMW(0); break;   // a count not listed: wait for everything (safe)
-#undef MOE_VMW_CASE
-#undef MOE_VMW
-      }
+    auto wait_steady = [&]() {
+      if (x_wave) MOE_VMW((D - 1) * NXW); else MOE_VMW((D - 1) * NW);
     };
+    auto wait_all = [&]() { MOE_VMW(0); };
+#undef MOE_VMW
     (void)XLW;
     for (int st = 0; st < D; ++st)
       if (st < nk) dma(st, st);
-    wait_steps(min(D, nk) - 1);
+    if (nk > D - 1) wait_steady(); else wait_all();
     __builtin_amdgcn_s_barrier();
     int b0 = 0;
     for (int kt = 0; kt < nk; ++kt) {
       const int bd = b0 == 0 ? NBUF - 1 : b0 - 1;   // (kt + D) % NBUF
-      if (kt + D < nk) dma(kt + D, bd);
+      // 0: no load this step, 1: a full K step, 2: the ragged last K step
+      const int dmode = kt + D < nk ? ((kt + D + 1) * BK > p.K ? 2 : 1) : 0;
+      auto load_i = [&](int i) {
+        if (dmode == 1) dma_one(std::false_type{}, kt + D, bd, i);
+        else if (dmode == 2) dma_one(std::true_type{}, kt + D, bd, i);
+      };
       const u32x4* const rx = sX[b0];
       const u32x4* const rw = sW[b0];
       Ops sa, sb;
@@ -464,14 +487,14 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) grouped_gemm_ker
 #pragma unroll
       for (int kk = 0; kk < KSTEPS; kk += 2) {
         if (kk + 1 < KSTEPS) read_ops(rx, rw, kk + 1, sb);
-        mfmas(sa);
+        mfmas_spread(sa, kk, load_i);
         if (kk + 2 < KSTEPS) read_ops(rx, rw, kk + 2, sa);
-        if (kk + 1 < KSTEPS) mfmas(sb);
+        if (kk + 1 < KSTEPS) mfmas_spread(sb, kk + 1, load_i);
       }
       if (kt + 1 < nk) {
         // this thread's part of step kt + 1 has landed; steps kt + 2 .. kt + D
         // (those issued) may still be in flight
-        wait_steps(min(kt + D, nk - 1) - (kt + 1));
+        if (kt + D <= nk - 1) wait_steady(); else wait_all();
         __builtin_amdgcn_s_barrier();
       }
       b0 = b0 == NBUF - 1 ? 0 : b0 + 1;
@@ -604,15 +627,16 @@ hipError_t launch_bm(GemmParams p, hipStream_t s) {
 
 }  // namespace
 
-// Tile configurations per BLOCK_M (compile-time knobs, defaults tuned on MI355X).
+// Tile configurations per BLOCK_M (compile-time knobs, defaults tuned on MI355X):
+// BM, BNW, WAVES_M, WAVES_N, BK, NS, MINW, direct-to-LDS.
 #ifndef MOE_G128
-#define MOE_G128 128, 256, 2, 2, 32, 3, 2, true
+#define MOE_G128 128, 256, 2, 4, 64, 3, 1, true
 #endif
 #ifndef MOE_G64
-#define MOE_G64 64, 256, 1, 4, 32, 3, 2, true
+#define MOE_G64 64, 256, 2, 4, 64, 2, 2, true
 #endif
 #ifndef MOE_G32
-#define MOE_G32 32, 256, 1, 4, 32, 3, 2, true
+#define MOE_G32 32, 256, 2, 4, 64, 2, 2, true
 #endif
 #ifndef MOE_G16
 #define MOE_G16 16, 128, 1, 4, 64, 3, 2, true
