@@ -141,7 +141,7 @@ __device__ __forceinline__ void expert_run(const int* __restrict__ expert_ids, i
 // SW: the tile's first BNW/2 weight rows are gate rows n0.., the rest the up
 // rows I+n0.. of the same act columns, and the epilogue is SwiGLU.
 template <int BM, int BNW, int WAVES_M, int WAVES_N, bool SW, int BK, int NS, int MINW, bool DMA>
-__global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) grouped_gemm_kernel(GemmParams p) {
+__global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) grouped_gemm_kernel(GemmParams pin) {
   constexpr int NT = 64 * WAVES_M * WAVES_N;   // threads of the workgroup
   constexpr int CPR = BK / 8;
   constexpr int WM = BM / WAVES_M;
@@ -176,8 +176,27 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) grouped_gemm_ker
   // ---- tile of this workgroup: XCD-contiguous; the tiles of each expert's
   // run of m-blocks are consecutive, in chunks of GM m-blocks with the n-tile
   // outer, so that neighbouring workgroups share weight tiles and token rows
-  const int ntn = p.ntiles_n, nmb = p.mblocks;
-  const int t = xcd_tile(blockIdx.x, ntn * nmb);
+  const int ntn = pin.ntiles_n;
+  const int tg = xcd_tile(blockIdx.x, ntn * (pin.mblocks + pin.nsb));
+  // tiles past the routed ones belong to the dense second part
+  const bool second = tg >= ntn * pin.mblocks;
+  GemmParams p = pin;
+  if (second) {
+    p.A = pin.A2;
+    p.W = pin.W2;
+    p.E = 1;
+    p.a_row_div = 0;
+    p.sorted_ids = nullptr;
+    p.expert_ids = nullptr;
+    p.ntpp = nullptr;
+    p.M = pin.M2;
+    p.a_rows = pin.M2;
+    p.C = pin.C2;
+    p.c_row_offset = pin.c2_row_offset;
+    p.topk_w = nullptr;
+  }
+  const int nmb = second ? pin.nsb : pin.mblocks;
+  const int t = second ? tg - ntn * pin.mblocks : tg;
   const int total_rows = p.ntpp ? *p.ntpp : p.M;
   const int vb = min(nmb, (total_rows + BM - 1) / BM);   // m-blocks holding rows
   const int mb0 = t / ntn;
@@ -613,8 +632,9 @@ hipError_t launch_bm(GemmParams p, hipStream_t s) {
   const int ncols = sw ? p.I : p.N;
   const int tile_n = sw ? BNW / 2 : BNW;
   p.mblocks = (p.M + BM - 1) / BM;
+  p.nsb = p.M2 > 0 ? (p.M2 + BM - 1) / BM : 0;
   p.ntiles_n = (ncols + tile_n - 1) / tile_n;
-  const int64_t nwg = (int64_t)p.mblocks * p.ntiles_n;
+  const int64_t nwg = (int64_t)(p.mblocks + p.nsb) * p.ntiles_n;
   if (nwg == 0) return hipSuccess;
   if (sw)
     hipLaunchKernelGGL((grouped_gemm_kernel<BM, BNW, WAVES_M, WAVES_N, true, BK, NS, MINW, DMA>),

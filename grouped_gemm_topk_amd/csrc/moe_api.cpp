@@ -353,21 +353,14 @@ int moe_fused_forward(const moe_layer_params* p, const void* x, const float* rou
   g1.c_fp32 = 0;
   g1.ldc = I;
   g1.a_rows = T;
+  if (p->n_shared) {   // the shared expert's tiles ride in the same launch
+    g1.A2 = (const uint16_t*)x;
+    g1.W2 = (const uint16_t*)shared_w13;
+    g1.M2 = T;
+    g1.C2 = L.act_sh;
+  }
   e = moe::launch_grouped_gemm(g1, bm, s);
   if (e != hipSuccess) return hip_status(e);
-  if (p->n_shared) {
-    moe::GemmParams gs = g1;
-    gs.W = (const uint16_t*)shared_w13;
-    gs.E = 1;
-    gs.a_row_div = 0;
-    gs.sorted_ids = nullptr;
-    gs.expert_ids = nullptr;
-    gs.ntpp = nullptr;
-    gs.M = T;
-    gs.C = L.act_sh;
-    e = moe::launch_grouped_gemm(gs, bm, s);
-    if (e != hipSuccess) return hip_status(e);
-  }
 
   // ---- GEMM2 + routed weight, scattered to slot rows of yslot
   moe::GemmParams g2{};
@@ -390,23 +383,15 @@ int moe_fused_forward(const moe_layer_params* p, const void* x, const float* rou
   g2.c_row_offset = 0;
   g2.ldc = H;
   g2.a_rows = (int)cap;
+  if (p->n_shared) {   // shared-expert rows T*k + t, weight 1, same launch
+    g2.A2 = L.act_sh;
+    g2.W2 = (const uint16_t*)shared_w2;
+    g2.M2 = T;
+    g2.C2 = L.yslot;
+    g2.c2_row_offset = n;
+  }
   e = moe::launch_grouped_gemm(g2, bm, s);
   if (e != hipSuccess) return hip_status(e);
-  if (p->n_shared) {
-    moe::GemmParams gs = g2;
-    gs.A = L.act_sh;
-    gs.W = (const uint16_t*)shared_w2;
-    gs.E = 1;
-    gs.sorted_ids = nullptr;
-    gs.expert_ids = nullptr;
-    gs.ntpp = nullptr;
-    gs.M = T;
-    gs.topk_w = nullptr;
-    gs.c_row_offset = n;
-    gs.a_rows = T;
-    e = moe::launch_grouped_gemm(gs, bm, s);
-    if (e != hipSuccess) return hip_status(e);
-  }
 
   // ---- combine
   e = moe::launch_combine(L.yslot, T, k, H, p->n_shared, out, s);

@@ -59,7 +59,16 @@ struct GemmParams {
   int64_t c_row_offset;     // weighted scatter: added to the destination row
   int ldc;                  // output row stride in elements
   int a_rows;               // rows of A (bounds of its buffer descriptor)
-  int mblocks, ntiles_n;    // tile grid (set by the launcher)
+  // optional dense second part with the same N, K and epilogue (the shared
+  // expert): M2 token rows of A2 times W2 [N, K] into C2 (store epilogues: row
+  // = token; weighted scatter: row c2_row_offset + token, weight 1).  Its
+  // tiles follow the routed ones in the same launch.  M2 = 0: none.
+  const uint16_t* A2;
+  const uint16_t* W2;
+  int M2;
+  void* C2;
+  int64_t c2_row_offset;
+  int mblocks, nsb, ntiles_n;   // tile grid: routed and second-part m-blocks (set by the launcher)
 };
 
 // ---------------------------------------------------------------- decode GEMVs
