@@ -137,7 +137,7 @@ __device__ __forceinline__ void expert_run(const int* __restrict__ expert_ids, i
 
 // BM token rows x BNW weight rows per workgroup tile, WAVES_M x WAVES_N waves,
 // BK-wide K steps, NS LDS stages (direct path: loads for step kt + NS - 1 are
-// issued while step kt is computed), MINW workgroups per CU requested.
+// issued while step kt is computed), MINW waves per SIMD requested (the launch bound).
 // SW: the tile's first BNW/2 weight rows are gate rows n0.., the rest the up
 // rows I+n0.. of the same act columns, and the epilogue is SwiGLU.
 template <int BM, int BNW, int WAVES_M, int WAVES_N, bool SW, int BK, int NS, int MINW, bool DMA>
@@ -653,10 +653,10 @@ hipError_t launch_bm(GemmParams p, hipStream_t s) {
 #define MOE_G128 128, 256, 2, 4, 64, 3, 1, true
 #endif
 #ifndef MOE_G64
-#define MOE_G64 64, 256, 2, 4, 64, 2, 2, true
+#define MOE_G64 64, 256, 2, 4, 64, 2, 4, true
 #endif
 #ifndef MOE_G32
-#define MOE_G32 32, 256, 2, 4, 64, 2, 2, true
+#define MOE_G32 32, 256, 2, 4, 64, 2, 4, true
 #endif
 #ifndef MOE_G16
 #define MOE_G16 16, 128, 1, 4, 64, 3, 2, true
