@@ -153,7 +153,7 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) grouped_gemm_ker
   constexpr int FN = WNW / MT;
   constexpr int XL = (BM * CPR + NT - 1) / NT;
   constexpr int WL = BNW * CPR / NT;
-  static_assert(WAVES_M * WAVES_N == 4 || WAVES_M * WAVES_N == 8, "4 or 8 waves");
+  static_assert(WAVES_M * WAVES_N >= 4 && WAVES_M * WAVES_N <= 8, "4 to 8 waves");
   static_assert(!SW || FN % 2 == 0, "SwiGLU pairs gate and up subtiles");
   static_assert(BNW * CPR % NT == 0, "weight tile load");
   static_assert(KSTEPS >= 1, "K step");
@@ -380,7 +380,9 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) grouped_gemm_ker
         : "memory");
   };
   // waves whose X part of the tile is empty (BM * CPR < 256) issue no X load
-  const bool x_wave = 64 * wave < BM * CPR;
+  // this wave issues the last of the XL token-row loads (waves past the end of
+  // the token tile skip it)
+  const bool x_wave = NT * (XL - 1) + 64 * wave < BM * CPR;
   // load i (of XL + WL per thread) of K step kt into LDS buffer b: the first
   // XL are token-row chunks, the rest weight-row chunks; the ragged last K
   // step (tail) masks the 16-byte chunks beyond K
@@ -472,8 +474,8 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) grouped_gemm_ker
     // vmcnt(n) with the other counters left alone; n = loads one thread
     // issues per K step (a compile-time count per kind of wave)
     constexpr int NXW = XL + WL;
-    constexpr int NW = WL + (XL > 1 ? XL - 1 : 0);
-    static_assert(BM * CPR % NT == 0 || XL == 1, "X loads per wave are all-or-one");
+    constexpr int NW = WL + XL - 1;
+    static_assert((BM * CPR - NT * (XL - 1)) % 64 == 0, "the last token-row load is whole waves");
     constexpr int D = NBUF - 1;   // prefetch distance in K steps
     static_assert((D - 1) * NXW <= 63, "vmcnt range");
     // wait until this thread's loads of the oldest pending step have landed;
