@@ -159,6 +159,15 @@ SMALL = [
     W.small_config("small_relu2_t16", T=16, H=264, I=40, E=32, top_k=6, activation=W.ACT_RELU2),
     W.small_config("small_t17_gemm", T=17, H=64, I=48, E=8, top_k=2),
     W.small_config("small_decode_ragged_k", T=3, H=600, I=328, E=64, top_k=8),
+    # the largest expert count and top-k the ABI accepts, on both paths
+    W.small_config("small_max_e_k", T=20, H=64, I=32, E=256, top_k=16),
+    W.small_config("small_max_e_k_decode", T=4, H=64, I=32, E=256, top_k=16),
+    # one expert: the layer is a dense MLP with weight 1
+    W.small_config("small_e1", T=24, H=64, I=40, E=1, top_k=1),
+    W.small_config("small_e1_decode", T=2, H=64, I=40, E=1, top_k=1),
+    # grouping that keeps every group (no restriction), with a shared expert
+    W.small_config("small_groups_all", T=30, H=64, I=48, E=16, top_k=3,
+                   scoring=W.SCORE_SIGMOID, n_group=4, topk_group=4, n_shared=1),
 ]
 
 
@@ -170,6 +179,22 @@ def test_fused_forward_small(moe, cfg, bm):
     ref = O.moe_forward_cfg(cfg if bm is None else dataclasses.replace(cfg, block_m=bm), inp)
     out, routing = _run_fused(moe, cfg, inp, bm)
     _check_routing(routing, ref, cfg.T, cfg.top_k, bm or cfg.block_m)
+    assert_out_close(out, ref["out"], cfg.name)
+
+
+@pytest.mark.parametrize("T", [6, 150])
+def test_fused_forward_one_hot_expert(moe, T):
+    """Every token's first choice is the same expert: one long run of blocks
+    for that expert, the second choices spread over the rest."""
+    cfg = W.small_config(f"one_hot_{T}", T=T, H=64, I=48, E=16, top_k=2, block_m=16)
+    print(f"fused {cfg.name}", flush=True)
+    inp = W.make_inputs(cfg)
+    inp["logits"] = inp["logits"].copy()
+    inp["logits"][:, 5] += 50.0
+    ref = O.moe_forward_cfg(cfg, inp)
+    assert np.all(ref["topk_ids"][:, 0] == 5)
+    out, routing = _run_fused(moe, cfg, inp)
+    _check_routing(routing, ref, cfg.T, cfg.top_k, cfg.block_m)
     assert_out_close(out, ref["out"], cfg.name)
 
 
