@@ -77,7 +77,10 @@ def _layer(cfg, inp, torch, moe, routing=False, weights=None):
                           routing_outputs=routing), w
 
 
-def time_layer(layer, steps, warmup, torch):
+def time_layer(layer, steps, warmup, torch, spread=False):
+    """Mean ms per step over `steps` back-to-back calls (events around the
+    whole run), the wall time, and with `spread` the p10/p50/p90 of per-step
+    event pairs (a second timed run, so the first stays free of them)."""
     for _ in range(warmup):
         layer.run()
     torch.cuda.synchronize()
@@ -91,7 +94,17 @@ def time_layer(layer, steps, warmup, torch):
     e1.record(s)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return e0.elapsed_time(e1) / steps, wall
+    mean = e0.elapsed_time(e1) / steps
+    if not spread:
+        return mean, wall, None
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(s)
+    for i in range(steps):
+        layer.run()
+        ev[i + 1].record(s)
+    torch.cuda.synchronize()
+    per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])
+    return mean, wall, {q: round(float(np.percentile(per, int(q[1:]))), 4) for q in ("p10", "p50", "p90")}
 
 
 def time_dominant_gemm(cfg, layer, steps, warmup, torch, moe):
@@ -168,6 +181,45 @@ def decode_case(name, torch, moe, W, O, reps=20):
             "alg_bytes": int(alg_bytes), "GBps": round(gbs, 1),
             "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "layers_cycled": nlayers,
             "max_abs_err": err}
+
+
+_ONE_THREAD = r"""
+import json, sys, time
+sys.path.insert(0, sys.argv[1])
+from grouped_gemm_topk_amd import workloads as W
+from oracle import moe_oracle as O
+cfg = W.CONFIGS[sys.argv[2]]
+ntok = int(sys.argv[3])
+inp = W.make_inputs(cfg)
+inp["x"] = inp["x"][:ntok]
+inp["logits"] = inp["logits"][:ntok]
+reps, t0 = 0, time.perf_counter()
+while True:
+    O.moe_forward_cfg(cfg, inp)
+    reps += 1
+    dt = time.perf_counter() - t0
+    if dt >= float(sys.argv[4]) or reps >= 50:
+        break
+print(json.dumps({"reps": reps, "seconds": dt}))
+"""
+
+
+def cpu_baseline_one_thread(cfg, ntok, min_seconds=10.0):
+    """The same oracle in a child process whose BLAS runs one thread (the
+    thread counts are fixed before numpy loads)."""
+    import subprocess
+    env = dict(os.environ)
+    for v in ("OPENBLAS_NUM_THREADS", "OMP_NUM_THREADS", "MKL_NUM_THREADS"):
+        env[v] = "1"
+    env["HIP_VISIBLE_DEVICES"] = ""   # the child never needs the GPU
+    r = subprocess.run([sys.executable, "-c", _ONE_THREAD, ROOT, cfg.name, str(ntok),
+                        str(min_seconds)], env=env, capture_output=True, text=True, timeout=600)
+    if r.returncode != 0:
+        return {"error": r.stderr.strip().splitlines()[-1:] if r.stderr else "failed"}
+    d = json.loads(r.stdout.strip().splitlines()[-1])
+    flops = cfg.flops() * ntok / cfg.T * d["reps"]
+    return {"value": round(flops / d["seconds"] / 1e12, 6), "unit": "TFLOPS", "cores": 1,
+            "sample": f"{d['reps']} x the first {ntok} of {cfg.T} tokens ({d['seconds']:.2f} s)"}
 
 
 def cpu_baseline(cfg, inp, ntok, W, O, min_seconds=10.0):
@@ -253,7 +305,7 @@ def main():
     layer.run()
     torch.cuda.synchronize()
     print(f"# {cfg.name}: inputs resident, timing {args.steps} steps", file=sys.stderr, flush=True)
-    ms, wall = time_layer(layer, args.steps, args.warmup, torch)
+    ms, wall, spread = time_layer(layer, args.steps, args.warmup, torch, spread=True)
     flops = cfg.flops()
     tflops = flops / (ms * 1e-3) / 1e12
     # dominant kernel: routed SwiGLU grouped GEMM
@@ -275,7 +327,8 @@ def main():
                    "block_m": cfg.block_m, "flops_per_step": flops,
                    "routed_only_TFLOPS": round(cfg.flops(routed_only=True) / (ms * 1e-3) / 1e12, 2),
                    "mfma_frac_of_layer": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                   "wall_s_timed": round(wall, 3)},
+                   "wall_s_timed": round(wall, 3),
+                   "step_ms_spread": spread},
         "roofline": {"bound": "mfma", "kernel": "grouped_gemm_kernel<128, 256, 2, 4, true, 64, 3, 1, true> (routed W13 + SwiGLU)",
                      "achieved": round(gemm_tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tf / MFMA_BF16_PEAK_TFLOPS, 4),
@@ -295,13 +348,14 @@ def main():
             c2 = W.CONFIGS[name]
             i2 = W.make_inputs(c2)
             l2, _ = _layer(c2, i2, torch, moe)
-            ms2, _ = time_layer(l2, args.steps, args.warmup, torch)
+            ms2, _, _ = time_layer(l2, args.steps, args.warmup, torch)
             line["extra"][name] = {"ms": round(ms2, 4),
                                    "TFLOPS": round(c2.flops() / (ms2 * 1e-3) / 1e12, 2)}
             del l2
             torch.cuda.empty_cache()
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(cfg, inp, min(args.cpu_tokens, cfg.T), W, O)
+        line["cpu_baseline"]["single_thread"] = cpu_baseline_one_thread(cfg, min(512, cfg.T))
     print(json.dumps(line), flush=True)
 
 
