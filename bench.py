@@ -329,7 +329,7 @@ def main():
                    "mfma_frac_of_layer": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                    "wall_s_timed": round(wall, 3),
                    "step_ms_spread": spread},
-        "roofline": {"bound": "mfma", "kernel": "grouped_gemm_kernel<128, 256, 2, 4, true, 64, 3, 1, true> (routed W13 + SwiGLU)",
+        "roofline": {"bound": "mfma", "kernel": "grouped_gemm_kernel<128, 256, 2, 4, true, 64, 3, 1> (routed W13 + SwiGLU)",
                      "achieved": round(gemm_tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tf / MFMA_BF16_PEAK_TFLOPS, 4),
                      "traffic": dominant_traffic(cfg.name),

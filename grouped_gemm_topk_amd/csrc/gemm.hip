@@ -99,12 +99,6 @@ __device__ __forceinline__ int swz(int r, int c) {
   return r * CPR + (c ^ ((r / (16 / CPR)) % CPR));
 }
 
-// Buffer descriptor (gfx9 raw buffer, 32-bit data) over `bytes` bytes; a load
-// whose offset is at or beyond `bytes` returns zero.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
-}
-
 #ifndef MOE_GM
 #define MOE_GM 8   // m-blocks per tile chunk
 #endif
@@ -140,7 +134,7 @@ __device__ __forceinline__ void expert_run(const int* __restrict__ expert_ids, i
 // issued while step kt is computed), MINW waves per SIMD requested (the launch bound).
 // SW: the tile's first BNW/2 weight rows are gate rows n0.., the rest the up
 // rows I+n0.. of the same act columns, and the epilogue is SwiGLU.
-template <int BM, int BNW, int WAVES_M, int WAVES_N, bool SW, int BK, int NS, int MINW, bool DMA>
+template <int BM, int BNW, int WAVES_M, int WAVES_N, bool SW, int BK, int NS, int MINW>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) grouped_gemm_kernel(GemmParams pin) {
   constexpr int NT = 64 * WAVES_M * WAVES_N;   // threads of the workgroup
   constexpr int CPR = BK / 8;
@@ -158,14 +152,11 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) grouped_gemm_ker
   static_assert(BNW * CPR % NT == 0, "weight tile load");
   static_assert(KSTEPS >= 1, "K step");
 
-  // LDS stages: three for the register-staged path; NS for the direct path
-  // (loads run NS - 1 K steps ahead)
-  constexpr int NBUF = DMA ? NS : 3;
-  static_assert(!DMA || NS >= 2, "direct-to-LDS pipeline needs two or more stages");
+  // LDS stages (loads run NS - 1 K steps ahead)
+  constexpr int NBUF = NS;
+  static_assert(NS >= 2, "the load pipeline needs two or more stages");
   __shared__ u32x4 sX[NBUF][BM * CPR];
   __shared__ u32x4 sW[NBUF][BNW * CPR];
-  auto bufx = [&](int b) { return sX[b]; };
-  auto bufw = [&](int b) { return sW[b]; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -217,57 +208,16 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) grouped_gemm_ker
   const uint16_t* We = p.W + (int64_t)e * p.N * p.K;
   const int ncols = SW ? p.I : p.N;           // output columns
   const int n0 = nt * (SW ? BNW / 2 : BNW);
-  const __amdgpu_buffer_rsrc_t xr_rs = make_rsrc(p.A, (int64_t)p.a_rows * p.K * 2);
-  const __amdgpu_buffer_rsrc_t wr_rs = make_rsrc(We, (int64_t)p.N * p.K * 2);
 
-  // ---- per-thread byte offsets of the source rows; kNoRow (beyond every
-  // descriptor even after the K advance is added) reads zeros
+  // kNoRow: an offset beyond every descriptor even after the K advance is
+  // added, so the load reads zeros
   constexpr int kNoRow = 0x7fff0000;
-  int xoff[XL], xsa[XL], xch[XL];
-#pragma unroll
-  for (int q = 0; q < XL; ++q) {
-    const int idx = tid + NT * q;
-    const int row = idx / CPR;
-    xch[q] = idx % CPR;
-    xsa[q] = swz<CPR>(row, xch[q]);
-    xoff[q] = kNoRow;
-    if (idx < BM * CPR) {
-      const int i = m0 + row;
-      int arow = -1;
-      if (p.sorted_ids) {
-        const int sid = p.sorted_ids[i];
-        if (sid >= 0 && sid < p.num_valid) arow = p.a_row_div ? sid / p.a_row_div : i;
-      } else if (i < p.M) {
-        arow = i;
-      }
-      if (arow >= 0) xoff[q] = arow * p.K * 2 + xch[q] * 16;
-    }
-  }
-  int woff[WL], wsa[WL], wch[WL];
-#pragma unroll
-  for (int q = 0; q < WL; ++q) {
-    const int idx = tid + NT * q;
-    const int r = idx / CPR;
-    wch[q] = idx % CPR;
-    wsa[q] = swz<CPR>(r, wch[q]);
-    int g;
-    bool ok;
-    if (SW) {
-      const int c = r < BNW / 2 ? n0 + r : n0 + r - BNW / 2;
-      ok = c < p.I;
-      g = r < BNW / 2 ? c : p.I + c;
-    } else {
-      g = n0 + r;
-      ok = g < p.N;
-    }
-    woff[q] = ok ? g * p.K * 2 + wch[q] * 16 : kNoRow;
-  }
 
   // ---- direct-to-LDS: lane l of a wave load fills LDS unit (base + l); the
   // unit at (row r, position pos) holds global chunk pos ^ mask(r), so the
   // source offsets carry the swizzle and each row's lanes still read one line
   int xdo[XL], wdo[WL];
-  if (DMA) {
+  {
 #pragma unroll
     for (int q = 0; q < XL; ++q) {
       const int u = tid + NT * q;
@@ -331,29 +281,6 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) grouped_gemm_ker
 #pragma unroll
       for (int v = 0; v < M::kVals; ++v) acc[f][q][v] = 0.f;
 
-  u32x4 xr[XL], wr[WL];
-  // loads of K step kt: the K advance rides in the scalar offset
-  auto gload = [&](int kt) {
-    const int k0b = kt * BK * 2;
-#pragma unroll
-    for (int q = 0; q < XL; ++q) xr[q] = __builtin_amdgcn_raw_buffer_load_b128(xr_rs, xoff[q], k0b, 0);
-#pragma unroll
-    for (int q = 0; q < WL; ++q) wr[q] = __builtin_amdgcn_raw_buffer_load_b128(wr_rs, woff[q], k0b, 0);
-  };
-  // the last K step when K % BK != 0: chunks past K read zeros
-  auto gload_tail = [&](int kt) {
-    const int k0 = kt * BK;
-#pragma unroll
-    for (int q = 0; q < XL; ++q) {
-      const int off = k0 + xch[q] * 8 < p.K ? xoff[q] + k0 * 2 : kNoRow;
-      xr[q] = __builtin_amdgcn_raw_buffer_load_b128(xr_rs, off, 0, 0);
-    }
-#pragma unroll
-    for (int q = 0; q < WL; ++q) {
-      const int off = k0 + wch[q] * 8 < p.K ? woff[q] + k0 * 2 : kNoRow;
-      wr[q] = __builtin_amdgcn_raw_buffer_load_b128(wr_rs, off, 0, 0);
-    }
-  };
   // direct-to-LDS loads of K step kt into LDS buffer b.  Issued from inline
   // asm (buffer_load_dwordx4 ... lds; M0 holds the wave's LDS destination and
   // is restored) so that the compiler, which cannot tell the in-flight
@@ -379,7 +306,6 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) grouped_gemm_ker
         : "s"(la), "v"(voff), "s"(rs), "s"(soff)
         : "memory");
   };
-  // waves whose X part of the tile is empty (BM * CPR < 256) issue no X load
   // this wave issues the last of the XL token-row loads (waves past the end of
   // the token tile skip it)
   const bool x_wave = NT * (XL - 1) + 64 * wave < BM * CPR;
@@ -411,15 +337,6 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) grouped_gemm_ker
     if ((kt + 1) * BK > p.K) dma_step(std::true_type{}, kt, b);
     else dma_step(std::false_type{}, kt, b);
   };
-  // DMA instructions one thread issues per K step
-  constexpr int XLW = (BM * CPR) / NT > 0 ? (BM * CPR) / NT : 1;
-  auto sstore = [&](u32x4* sx, u32x4* sw) {
-#pragma unroll
-    for (int q = 0; q < XL; ++q)
-      if (tid + NT * q < BM * CPR) sx[xsa[q]] = xr[q];
-#pragma unroll
-    for (int q = 0; q < WL; ++q) sw[wsa[q]] = wr[q];
-  };
   // operand registers of one k-substep
   struct Ops {
     bf16x8 b[FM], a[FN];
@@ -429,12 +346,6 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) grouped_gemm_ker
     for (int q = 0; q < FM; ++q) o.b[q] = __builtin_bit_cast(bf16x8, sx[xb[kk] + q * MT * CPR]);
 #pragma unroll
     for (int f = 0; f < FN; ++f) o.a[f] = __builtin_bit_cast(bf16x8, sw[wb[kk] + wsub_off(f) * CPR]);
-  };
-  auto mfmas = [&](const Ops& o) {
-#pragma unroll
-    for (int f = 0; f < FN; ++f)
-#pragma unroll
-      for (int q = 0; q < FM; ++q) acc[f][q] = M::run(o.a[f], o.b[q], acc[f][q]);
   };
   // the MFMAs of substep kk with this thread's loads of a later K step spread
   // between them: load i follows MFMA i * TM / ND of the step, so the address
@@ -455,22 +366,13 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) grouped_gemm_ker
   };
 
   // ---- pipeline over K steps, one barrier per step.
-  // Direct path (NBUF = NS buffers, D = NS - 1): step kt computes from buffer
+  // NBUF = NS buffers, D = NS - 1: step kt computes from buffer
   // kt % NBUF while its MFMAs interleave the loads of step kt + D into the
   // buffer that step kt - 1 used (every wave is past the barrier that ended
   // step kt - 1); then each thread waits for its own loads of step kt + 1 and
   // the barrier makes them visible to all waves.
-  // Register path (three buffers): step kt stores step kt + 1 (loaded during
-  // step kt - 1) into buffer (kt + 1) % 3, requests step kt + 2, barrier, then
-  // the MFMAs of step kt with each k-substep's operands read one substep
-  // ahead; the first substep of step kt + 1 is read during the last MFMAs of
-  // step kt.
   const int nk = (p.K + BK - 1) / BK;
-  const bool ktail = p.K % BK != 0;
-  auto load_step = [&](int kt) {
-    if (ktail && kt == nk - 1) gload_tail(kt); else gload(kt);
-  };
-  if constexpr (DMA) {
+  {
     // vmcnt(n) with the other counters left alone; n = loads one thread
     // issues per K step (a compile-time count per kind of wave)
     constexpr int NXW = XL + WL;
@@ -487,7 +389,6 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) grouped_gemm_ker
     };
     auto wait_all = [&]() { MOE_VMW(0); };
 #undef MOE_VMW
-    (void)XLW;
     for (int st = 0; st < D; ++st)
       if (st < nk) dma(st, st);
     if (nk > D - 1) wait_steady(); else wait_all();
@@ -520,51 +421,6 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) grouped_gemm_ker
       }
       b0 = b0 == NBUF - 1 ? 0 : b0 + 1;
     }
-  } else {
-  load_step(0);
-  sstore(bufx(0), bufw(0));
-  if (nk > 1) load_step(1);
-  __syncthreads();
-  // two operand register sets used in turn: while the MFMAs of one substep
-  // read set A, the LDS reads of the next substep fill set B (no copies)
-  static_assert(KSTEPS % 2 == 0 || KSTEPS == 1, "substeps pair up");
-  Ops sa, sb;
-  read_ops(bufx(0), bufw(0), 0, sa);
-  int b0 = 0;   // buffer of step kt
-  for (int kt = 0; kt < nk; ++kt) {
-    const int b1 = b0 == NBUF - 1 ? 0 : b0 + 1;
-    if (kt + 1 < nk) sstore(bufx(b1), bufw(b1));
-    if (kt + 2 < nk) load_step(kt + 2);
-    __syncthreads();
-    const bool more = kt + 1 < nk;
-    if constexpr (KSTEPS == 1) {
-      // one substep per K step: alternate the sets across K steps
-      if (more) read_ops(bufx(b1), bufw(b1), 0, sb);
-      mfmas(sa);
-      ++kt;
-      b0 = b1;
-      if (kt >= nk) break;
-      const int b2 = b0 == NBUF - 1 ? 0 : b0 + 1;
-      if (kt + 1 < nk) sstore(bufx(b2), bufw(b2));
-      if (kt + 2 < nk) load_step(kt + 2);
-      __syncthreads();
-      if (kt + 1 < nk) read_ops(bufx(b2), bufw(b2), 0, sa);
-      mfmas(sb);
-      b0 = b2;
-    } else {
-#pragma unroll
-      for (int kk = 0; kk < KSTEPS; kk += 2) {
-        read_ops(bufx(b0), bufw(b0), kk + 1, sb);
-        mfmas(sa);
-        if (kk + 2 < KSTEPS)
-          read_ops(bufx(b0), bufw(b0), kk + 2, sa);
-        else if (more)
-          read_ops(bufx(b1), bufw(b1), 0, sa);
-        mfmas(sb);
-      }
-      b0 = b1;
-    }
-  }
   }
 
   // ---- epilogue
@@ -628,7 +484,7 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) grouped_gemm_ker
   }
 }
 
-template <int BM, int BNW, int WAVES_M, int WAVES_N, int BK, int NS, int MINW, bool DMA>
+template <int BM, int BNW, int WAVES_M, int WAVES_N, int BK, int NS, int MINW>
 hipError_t launch_bm(GemmParams p, hipStream_t s) {
   const bool sw = p.epi == 1;
   const int ncols = sw ? p.I : p.N;
@@ -639,10 +495,10 @@ hipError_t launch_bm(GemmParams p, hipStream_t s) {
   const int64_t nwg = (int64_t)(p.mblocks + p.nsb) * p.ntiles_n;
   if (nwg == 0) return hipSuccess;
   if (sw)
-    hipLaunchKernelGGL((grouped_gemm_kernel<BM, BNW, WAVES_M, WAVES_N, true, BK, NS, MINW, DMA>),
+    hipLaunchKernelGGL((grouped_gemm_kernel<BM, BNW, WAVES_M, WAVES_N, true, BK, NS, MINW>),
                        dim3((unsigned)nwg), dim3(64 * WAVES_M * WAVES_N), 0, s, p);
   else
-    hipLaunchKernelGGL((grouped_gemm_kernel<BM, BNW, WAVES_M, WAVES_N, false, BK, NS, MINW, DMA>),
+    hipLaunchKernelGGL((grouped_gemm_kernel<BM, BNW, WAVES_M, WAVES_N, false, BK, NS, MINW>),
                        dim3((unsigned)nwg), dim3(64 * WAVES_M * WAVES_N), 0, s, p);
   return hipGetLastError();
 }
@@ -650,18 +506,18 @@ hipError_t launch_bm(GemmParams p, hipStream_t s) {
 }  // namespace
 
 // Tile configurations per BLOCK_M (compile-time knobs, defaults tuned on MI355X):
-// BM, BNW, WAVES_M, WAVES_N, BK, NS, MINW, direct-to-LDS.
+// BM, BNW, WAVES_M, WAVES_N, BK, NS, MINW.
 #ifndef MOE_G128
-#define MOE_G128 128, 256, 2, 4, 64, 3, 1, true
+#define MOE_G128 128, 256, 2, 4, 64, 3, 1
 #endif
 #ifndef MOE_G64
-#define MOE_G64 64, 256, 2, 4, 64, 2, 4, true
+#define MOE_G64 64, 256, 2, 4, 64, 2, 4
 #endif
 #ifndef MOE_G32
-#define MOE_G32 32, 256, 2, 4, 64, 2, 4, true
+#define MOE_G32 32, 256, 2, 4, 64, 2, 4
 #endif
 #ifndef MOE_G16
-#define MOE_G16 16, 128, 1, 4, 64, 3, 2, true
+#define MOE_G16 16, 128, 1, 4, 64, 3, 2
 #endif
 
 hipError_t launch_grouped_gemm(const GemmParams& p, int block_m, hipStream_t s) {
