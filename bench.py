@@ -38,10 +38,10 @@ MALL_BYTES = 256 << 20           # Infinity Cache
 # digest; any other source reports traffic null until it is measured again.
 DOMINANT_TRAFFIC = {
     "src": "grouped_gemm_topk_amd/csrc/gemm.hip",
-    "sha256": "cb5860ced3ab2c08e49e91706c93a76a9cc72df02bcdd383b5038cc5b4b25362",
+    "sha256": "0154cf8966bf34e05af79856beda3a2c23b0a0cda574295a156130c29f5c7790",
     "config": "dsv3",
-    "fetch_bytes": 1320034713,
-    "write_bytes": 89789337,
+    "fetch_bytes": 1298403123,
+    "write_bytes": 89789132,
 }
 
 
