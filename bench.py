@@ -9,9 +9,12 @@ resident in HBM before timing starts.
 Prints ONE JSON line: TFLOPS of the layer (2*T*k_eff*3*H*I / latency), the
 roofline entry of the dominant kernel (the SwiGLU grouped GEMM, timed alone
 with HIP events on its stream), decode microseconds per layer at T = 1, 3, 8
-(128 experts top-8, cycling through enough distinct layers that the 256 MB
-Infinity Cache cannot hold the touched weights), and the CPU oracle's rate on
-a bounded sample of the same workload.
+(128 experts top-8) and of the squared-ReLU layer at T = 1, 16, each cycling
+through enough distinct layers that the 256 MB Infinity Cache cannot hold the
+touched weights and cross-checked with an explicit cache flush before every
+call, the achievable peaks of this GPU from the probe library's own MFMA-loop
+and streaming-read kernels, and the CPU oracle's rate on a bounded sample of
+the same workload.
 """
 from __future__ import annotations
 
@@ -30,6 +33,9 @@ import numpy as np  # noqa: E402
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 MALL_BYTES = 256 << 20           # Infinity Cache
+# decode-shaped layers (GEMV path): 128 experts top-8 SwiGLU at T = 1, 3, 8 and
+# the squared-ReLU layer (128 experts top-6) at T = 1, 16
+DECODE_CASES = ("decode_t1", "decode_t3", "decode_t8", "relu2_t1", "relu2_t16")
 
 # HBM-side bytes per launch of the dominant kernel (routed SwiGLU grouped GEMM
 # of the dsv3 layer) from two rocprofv3 counter passes: FETCH_SIZE x 2.0 and
@@ -53,6 +59,9 @@ def parse():
     ap.add_argument("--config", default="dsv3")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode measurements")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="only the decode measurements (one JSON line with them), for profiler passes")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the achievable-peak probes")
     ap.add_argument("--cpu-tokens", type=int, default=4096,
                     help="tokens of the workload the CPU oracle runs on")
     ap.add_argument("--extra", default="", help="comma list of more configs to time (report only)")
@@ -134,8 +143,11 @@ def time_dominant_gemm(cfg, layer, steps, warmup, torch, moe):
     return e0.elapsed_time(e1) / steps
 
 
-def decode_case(name, torch, moe, W, O, reps=20):
-    """µs per layer at decode shape, cycling L distinct copies of the weights."""
+def decode_case(name, torch, moe, W, O, reps=20, flush_reps=20):
+    """µs per layer at decode shape, cycling L distinct copies of the weights
+    from a captured graph; cross-checked by timing one layer eagerly with a
+    1 GiB copy (4 x the Infinity Cache) between calls, events around the layer
+    alone, so that every call starts with cold caches."""
     cfg = W.CONFIGS[name]
     inp = W.make_inputs(cfg)
     ids, _ = O.gate(inp["logits"], cfg.top_k, cfg.scoring, cfg.n_group, cfg.topk_group,
@@ -168,6 +180,22 @@ def decode_case(name, torch, moe, W, O, reps=20):
     e1.record()
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / (reps * nlayers)
+    del g
+    # cross-check: cold-cache calls of one layer, the flush queued ahead of them
+    fa = torch.empty(MALL_BYTES * 2 // 4, dtype=torch.float32, device="cuda")
+    fb = torch.empty_like(fa)
+    lay = layers[0]
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(flush_reps)]
+    for a, b in evs:
+        fb.copy_(fa)
+        a.record()
+        lay.run()
+        b.record()
+    torch.cuda.synchronize()
+    flushed = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+    us_flushed = flushed[len(flushed) // 2]
+    del fa, fb
     alg_bytes = wbytes + cfg.T * cfg.H * 2 + cfg.T * cfg.H * 4 + cfg.T * cfg.E * 4
     gbs = alg_bytes / (us * 1e-6) / 1e9
     # parity of the last layer's output against the oracle (all tokens)
@@ -177,7 +205,8 @@ def decode_case(name, torch, moe, W, O, reps=20):
     err = float(np.abs(out - ref).max())
     del layers, base
     torch.cuda.empty_cache()
-    return {"T": cfg.T, "us_per_layer": round(us, 2), "touched_experts": touched,
+    return {"config": name, "T": cfg.T, "us_per_layer": round(us, 2),
+            "us_flushed_median": round(us_flushed, 2), "touched_experts": touched,
             "alg_bytes": int(alg_bytes), "GBps": round(gbs, 1),
             "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "layers_cycled": nlayers,
             "max_abs_err": err}
@@ -249,6 +278,73 @@ def cpu_baseline(cfg, inp, ntok, W, O, min_seconds=10.0):
                       f"({dt:.2f} s, fp64 numpy per-expert loop incl. weight widening)"}
 
 
+def achievable_peaks(torch, reps=5):
+    """This GPU's achievable rates from the probe library (libmoe_probe.so,
+    built beside libmoe.so): dense bf16 MFMA TFLOP/s of a loop of independent
+    32x32x16 MFMAs with no memory traffic, and GB/s of a non-temporal
+    streaming read of 4 GiB.  Best of ``reps`` launches each."""
+    import ctypes
+    from grouped_gemm_topk_amd import build as B
+    if not os.path.exists(B.PROBE_LIB):
+        return {"error": "libmoe_probe.so is not built"}
+    L = ctypes.CDLL(B.PROBE_LIB)
+    L.moe_probe_mfma_loop.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    L.moe_probe_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
+                                     ctypes.c_void_p]
+    s = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(s.cuda_stream)
+
+    def best(launch):
+        launch()
+        times = []
+        for _ in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            launch()
+            e1.record(s)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) * 1e-3)
+        return min(times)
+
+    grid, iters = 1024, 2000   # 4 workgroups of 4 waves per CU
+    out = torch.empty(grid * 256, dtype=torch.float32, device="cuda")
+
+    def mf():
+        rc = L.moe_probe_mfma_loop(ctypes.c_void_p(out.data_ptr()), grid, iters, sp)
+        if rc:
+            raise RuntimeError(f"moe_probe_mfma_loop: hip error {rc}")
+    t = best(mf)
+    flops = grid * 4 * iters * L.moe_probe_mfma_flops_per_wave_iter()
+    nbytes = 4 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    rgrid = 1024
+    rout = torch.empty(rgrid * 256, dtype=torch.int32, device="cuda")
+
+    def rd():
+        rc = L.moe_probe_hbm_read(ctypes.c_void_p(buf.data_ptr()), nbytes,
+                                  ctypes.c_void_p(rout.data_ptr()), rgrid, sp)
+        if rc:
+            raise RuntimeError(f"moe_probe_hbm_read: hip error {rc}")
+    tr = best(rd)
+    del buf
+    torch.cuda.empty_cache()
+    return {"mfma_bf16_TFLOPS": round(flops / t / 1e12, 1), "hbm_read_GBps": round(nbytes / tr / 1e9, 1),
+            "how": f"best of {reps}: {grid} x 4 waves x {iters} rounds of 16 independent 32x32x16 bf16 "
+                   f"MFMAs; non-temporal 16 B/lane streaming read of {nbytes >> 30} GiB"}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def dominant_traffic(cfg_name):
     """Counter-derived bytes per launch, or None when the kernel source has
     changed since the counters were taken (or for another workload)."""
@@ -299,6 +395,10 @@ def main():
         copy_calibration(torch)
         return
     moe.lib()
+    if args.decode_only:
+        print(json.dumps({"decode": [decode_case(n, torch, moe, W, O) for n in DECODE_CASES]}),
+              flush=True)
+        return
     cfg = W.CONFIGS[args.config]
     inp = W.make_inputs(cfg)
     layer, _ = _layer(cfg, inp, torch, moe, routing=True)
@@ -338,9 +438,18 @@ def main():
                      "avg_launch_us": round(gemm_ms * 1e3, 2),
                      "alg_flops_per_launch": gemm_flops},
     }
+    peaks = None if args.no_peaks else achievable_peaks(torch)
+    if peaks and "mfma_bf16_TFLOPS" in peaks:
+        line["roofline"]["achievable_peak"] = peaks["mfma_bf16_TFLOPS"]
+        line["roofline"]["frac_of_achievable"] = round(gemm_tf / peaks["mfma_bf16_TFLOPS"], 4)
+        line["config"]["mfma_frac_of_achievable"] = round(tflops / peaks["mfma_bf16_TFLOPS"], 4)
+    if peaks:
+        line["achievable_peaks"] = peaks
     if not args.no_decode:
-        line["decode"] = [decode_case(n, torch, moe, W, O) for n in
-                          ("decode_t1", "decode_t3", "decode_t8")]
+        line["decode"] = [decode_case(n, torch, moe, W, O) for n in DECODE_CASES]
+        if peaks and "hbm_read_GBps" in peaks:
+            for d in line["decode"]:
+                d["frac_of_achievable_hbm"] = round(d["GBps"] / peaks["hbm_read_GBps"], 4)
     extra = [e for e in args.extra.split(",") if e]
     if extra:
         line["extra"] = {}
@@ -356,6 +465,7 @@ def main():
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(cfg, inp, min(args.cpu_tokens, cfg.T), W, O)
         line["cpu_baseline"]["single_thread"] = cpu_baseline_one_thread(cfg, min(512, cfg.T))
+        line["cpu_baseline"]["cpu_model"] = cpu_model()
     print(json.dumps(line), flush=True)
 
 
