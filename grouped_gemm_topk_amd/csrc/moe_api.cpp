@@ -210,7 +210,6 @@ int moe_grouped_gemm(const moe_gemm_args* args, void* workspace, size_t* workspa
   if (g.capacity == 0) return MOE_OK;
   if (!g.a || !g.w || !g.c || !g.sorted_token_ids || !g.expert_ids || !g.num_tokens_post_padded)
     return MOE_ERR_NULL;
-  if (g.epilogue == MOE_EPI_WEIGHTED_SCATTER && !g.topk_weights) return MOE_ERR_NULL;
   if (!aligned16(g.a) || !aligned16(g.w) || !aligned16(g.c)) return MOE_ERR_ALIGN;
   int st = check_device();
   if (st != MOE_OK) return st;

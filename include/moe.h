@@ -112,7 +112,13 @@ int moe_align(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E, int32_t 
  *     SWIGLU           C[i] = silu(h[:N/2]) * h[N/2:]             (N/2 columns)
  *     RELU2            C[i] = max(h, 0)^2                         (N columns)
  *     WEIGHTED_SCATTER C[s] = topk_weights[s] * h, only if s < num_valid
+ *                      (topk_weights NULL: weight 1, a plain scatter by slot)
  *   Row-ordered epilogues (STORE/SWIGLU/RELU2) write zero rows for pads.
+ *
+ * With top_k = 1 (moe_align over per-row expert indices) and WEIGHTED_SCATTER
+ * without weights this is the contiguous grouped GEMM of the axolotl page
+ * (`cg_grouped_gemm_forward`: output row i = input row i times the transposed
+ * weight of its expert), for any grouping of the rows.
  */
 typedef struct {
   const void* a;           /* bf16 A rows, row stride K                                  */
@@ -126,7 +132,7 @@ typedef struct {
   int32_t num_valid;       /* T * top_k                                                  */
   int32_t capacity;        /* entries of sorted_token_ids (multiple of block_m)          */
   int32_t epilogue;        /* MOE_EPI_*                                                  */
-  const float* topk_weights; /* [num_valid] for WEIGHTED_SCATTER                         */
+  const float* topk_weights; /* [num_valid] for WEIGHTED_SCATTER, or NULL (weight 1)     */
   void* c;                 /* output rows: capacity rows (row-ordered) or num_valid rows */
   int32_t c_is_fp32;       /* 1: fp32 output, 0: bf16 (round to nearest even)            */
 } moe_gemm_args;

@@ -17,7 +17,9 @@ Steps, in the order the skill card's *Token-Expert Routing* lists them:
 2. sort by expert and pad to BLOCK_M (``align``)
 3. per-expert MLP and routed-weight combine (``expert_loop``)
 
-plus ``grouped_gemm`` (one grouped GEMM over the aligned layout) and
+plus ``grouped_gemm`` (one grouped GEMM over the aligned layout),
+``indexed_grouped_gemm`` (the standalone contiguous grouped GEMM of the
+axolotl page, rows mapped to experts by an index per row) and
 ``moe_forward`` (the whole layer).
 
 Readings where the pages are silent (each is pinned by a test unless marked):
@@ -279,7 +281,8 @@ def grouped_gemm(a: np.ndarray, a_row_div: int, w: np.ndarray, sorted_token_ids:
 
     Epilogues: STORE h, SWIGLU silu(h[:N/2]) * h[N/2:], RELU2 max(h,0)^2 —
     written at row i, zero for pad rows; WEIGHTED_SCATTER writes
-    topk_weights[s] * h at row s = sorted_token_ids[i] for valid rows only.
+    topk_weights[s] * h at row s = sorted_token_ids[i] for valid rows only
+    (weight 1 when topk_weights is None: a plain scatter by slot).
     Rows at or beyond num_tokens_post_padded are not produced (NaN here).
     Returns float64.
     """
@@ -289,7 +292,8 @@ def grouped_gemm(a: np.ndarray, a_row_div: int, w: np.ndarray, sorted_token_ids:
     ncols = N // 2 if epilogue == EPI_SWIGLU else N
     if epilogue == EPI_WEIGHTED_SCATTER:
         c = np.full((num_valid, ncols), np.nan)
-        wf = np.asarray(topk_weights, dtype=np.float64).reshape(-1)
+        wf = (np.ones(num_valid) if topk_weights is None
+              else np.asarray(topk_weights, dtype=np.float64).reshape(-1))
     else:
         c = np.full((len(sorted_token_ids), ncols), np.nan)
     for i in range(num_tokens_post_padded):
@@ -315,6 +319,32 @@ def grouped_gemm(a: np.ndarray, a_row_div: int, w: np.ndarray, sorted_token_ids:
         else:
             raise ValueError("unknown epilogue")
     return c
+
+
+def indexed_grouped_gemm(x: np.ndarray, w: np.ndarray, expert_indices: np.ndarray,
+                         rows: Optional[np.ndarray] = None) -> np.ndarray:
+    """The contiguous grouped GEMM of the axolotl page (``cg_forward.py``,
+    ``cg_grouped_gemm_forward`` and its per-block ``pytorch_reference``):
+    output row i is input row i times the transposed weight of its expert,
+    ``x[i] @ w[expert_indices[i]].T``.  The page takes one index per block of
+    ``group_size_m`` rows and requires each block to share it; read per row,
+    the definition needs no such condition and agrees where it holds.
+
+    One matmul per expert over its rows, float64.  ``rows``: only these output
+    rows, in the given order (each computed alone; for spot checks of large
+    cases)."""
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    idx = np.asarray(expert_indices).reshape(-1)
+    if rows is not None:
+        return np.stack([w[int(idx[r])] @ x[r] for r in rows]) if len(rows) else \
+            np.zeros((0, w.shape[1]))
+    out = np.full((x.shape[0], w.shape[1]), np.nan)
+    for e in range(w.shape[0]):
+        sel = np.nonzero(idx == e)[0]
+        if sel.size:
+            out[sel] = x[sel] @ w[e].T
+    return out
 
 
 # ----------------------------------------------------------------------------

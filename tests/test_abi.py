@@ -158,6 +158,6 @@ def test_grouped_gemm_validation(L):
     assert call(E=0) == -2
     assert call(num_valid=7) == -2         # not a multiple of a_row_div
     assert call(a=None) == -1
-    assert call(epilogue=3) == -1          # weighted scatter needs weights
+    assert call(epilogue=3, capacity=0) == 0   # scatter without weights is valid (weight 1)
     assert call(w=fake + 8) == -5
     assert call(capacity=0) == 0           # nothing to do

@@ -387,3 +387,63 @@ def test_dsv3_small_shape_with_shared_vs_dense():
                             O.bf16_to_f64(inp["shared_w2"]))
     assert np.max(np.abs(res["out"] - ref)) <= 1e-4 * np.max(np.abs(ref))
     assert np.all(np.abs(res["topk_weights"].astype(np.float64).sum(1) - 2.5) <= 1e-5)
+
+
+# ---------------------------------------------------------------- indexed grouped GEMM
+def test_indexed_grouped_gemm_bruteforce():
+    """Every output element as a pure-Python sum over K (no matmul)."""
+    rng = np.random.default_rng(5)
+    M, K, N, E = 7, 5, 4, 3
+    x = rng.standard_normal((M, K))
+    w = rng.standard_normal((E, N, K))
+    idx = np.array([2, 0, 0, 1, 2, 2, 0])
+    got = O.indexed_grouped_gemm(x, w, idx)
+    for i in range(M):
+        for n in range(N):
+            s = 0.0
+            for kk in range(K):
+                s += float(x[i, kk]) * float(w[idx[i], n, kk])
+            assert abs(got[i, n] - s) <= 1e-12 * max(1.0, abs(s))
+    np.testing.assert_allclose(O.indexed_grouped_gemm(x, w, idx, rows=[6, 0]), got[[6, 0]],
+                               rtol=1e-14, atol=1e-14)
+
+
+def test_indexed_grouped_gemm_permutation_weights():
+    """W[e] a permutation matrix P_e (not symmetric): row i must come out as
+    P_e x[i] -- a transposed operand would give P_e^T x[i], a wrong expert
+    another permutation."""
+    rng = np.random.default_rng(6)
+    K = 6
+    perms = [rng.permutation(K) for _ in range(3)]
+    w = np.zeros((3, K, K))
+    for e, p in enumerate(perms):
+        w[e, np.arange(K), p] = 1.0          # (P_e x)[n] = x[p[n]]
+    x = rng.standard_normal((9, K))
+    idx = np.array([0, 1, 2, 2, 1, 0, 1, 1, 2])
+    got = O.indexed_grouped_gemm(x, w, idx)
+    for i in range(9):
+        assert np.array_equal(got[i], x[i, perms[idx[i]]])
+
+
+def test_indexed_grouped_gemm_row_permutation_equivariance():
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((20, 8))
+    w = rng.standard_normal((4, 6, 8))
+    idx = rng.integers(0, 4, 20)
+    p = rng.permutation(20)
+    np.testing.assert_allclose(O.indexed_grouped_gemm(x[p], w, idx[p]),
+                               O.indexed_grouped_gemm(x, w, idx)[p], rtol=1e-13, atol=1e-13)
+
+
+def test_indexed_grouped_gemm_equals_aligned_scatter():
+    """The library's composition: align the per-row indices with top_k = 1,
+    then the aligned grouped GEMM with a plain scatter by slot (weight 1)."""
+    rng = np.random.default_rng(8)
+    M, K, N, E, bm = 45, 16, 24, 5, 16
+    x = rng.standard_normal((M, K))
+    w = rng.standard_normal((E, N, K))
+    idx = np.repeat(np.arange(E), [0, 17, 3, 25, 0]).astype(np.int32)   # contiguous, uneven
+    al = O.align(idx.reshape(M, 1), E, bm)
+    via = O.grouped_gemm(x, 1, w, al["sorted_token_ids"], al["expert_ids"],
+                         al["num_tokens_post_padded"], bm, M, O.EPI_WEIGHTED_SCATTER, None)
+    np.testing.assert_allclose(via, O.indexed_grouped_gemm(x, w, idx), rtol=1e-12, atol=1e-12)
