@@ -12,7 +12,8 @@ with HIP events on its stream), decode microseconds per layer at T = 1, 3, 8
 (128 experts top-8) and of the squared-ReLU layer at T = 1, 16, each cycling
 through enough distinct layers that the 256 MB Infinity Cache cannot hold the
 touched weights and cross-checked with an explicit cache flush before every
-call, the achievable peaks of this GPU from the probe library's own MFMA-loop
+call, the standalone grouped GEMM at the four shapes of the axolotl page's
+benchmark table, the achievable peaks of this GPU from the probe library's own MFMA-loop
 and streaming-read kernels, and the CPU oracle's rate on a bounded sample of
 the same workload.
 """
@@ -62,6 +63,8 @@ def parse():
     ap.add_argument("--decode-only", action="store_true",
                     help="only the decode measurements (one JSON line with them), for profiler passes")
     ap.add_argument("--no-peaks", action="store_true", help="skip the achievable-peak probes")
+    ap.add_argument("--no-gemm-scenarios", action="store_true",
+                    help="skip the standalone grouped-GEMM scenarios")
     ap.add_argument("--cpu-tokens", type=int, default=4096,
                     help="tokens of the workload the CPU oracle runs on")
     ap.add_argument("--extra", default="", help="comma list of more configs to time (report only)")
@@ -278,6 +281,58 @@ def cpu_baseline(cfg, inp, ntok, W, O, min_seconds=10.0):
                       f"({dt:.2f} s, fp64 numpy per-expert loop incl. weight widening)"}
 
 
+def _event_ms(fn, steps, warmup, torch):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(steps):
+        fn()
+    e1.record(s)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def gemm_scenarios(steps, warmup, torch, moe, W):
+    """The contiguous grouped GEMM at the four shapes of the axolotl page's
+    benchmark table (uniform groups): the whole call (align of the per-row
+    indices + grouped GEMM) and the GEMM launch alone, plus hipBLASLt (one
+    torch.matmul per group on a contiguous transposed weight) as context."""
+    res = []
+    for sc in W.GEMM_SCENARIOS.values():
+        inp = W.make_gemm_inputs(sc)
+        x, w = _to_dev(inp["x"], torch), _to_dev(inp["w"], torch)
+        op = moe.IndexedGroupedGemm(x, w, _to_dev(inp["expert_indices"], torch), sc.block_m)
+        op.run()
+        ms_call = _event_ms(op.run, steps, warmup, torch)
+        ms_gemm = _event_ms(op.gemm, steps, warmup, torch)
+        gsz = sc.M // sc.G
+        wt = [w[g].t().contiguous() for g in range(sc.G)]
+        xs = [x[g * gsz:(g + 1) * gsz] for g in range(sc.G)]
+        ref_out = torch.empty((sc.M, sc.N), dtype=torch.bfloat16, device="cuda")
+        outs = [ref_out[g * gsz:(g + 1) * gsz] for g in range(sc.G)]
+
+        def blas():
+            for g in range(sc.G):
+                torch.matmul(xs[g], wt[g], out=outs[g])
+        ms_blas = _event_ms(blas, steps, warmup, torch)
+        f = sc.flops()
+        res.append({"scenario": sc.name, "G": sc.G, "M": sc.M, "N": sc.N, "K": sc.K,
+                    "block_m": sc.block_m, "ms": round(ms_call, 4),
+                    "TFLOPS": round(f / (ms_call * 1e-3) / 1e12, 1),
+                    "gemm_ms": round(ms_gemm, 4),
+                    "gemm_TFLOPS": round(f / (ms_gemm * 1e-3) / 1e12, 1),
+                    "mfma_frac": round(f / (ms_gemm * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                    "hipblaslt_per_group_ms": round(ms_blas, 4),
+                    "hipblaslt_per_group_TFLOPS": round(f / (ms_blas * 1e-3) / 1e12, 1)})
+        del op, x, w, wt, xs, outs, ref_out
+        torch.cuda.empty_cache()
+    return res
+
+
 def achievable_peaks(torch, reps=5):
     """This GPU's achievable rates from the probe library (libmoe_probe.so,
     built beside libmoe.so): dense bf16 MFMA TFLOP/s of a loop of independent
@@ -450,6 +505,8 @@ def main():
         if peaks and "hbm_read_GBps" in peaks:
             for d in line["decode"]:
                 d["frac_of_achievable_hbm"] = round(d["GBps"] / peaks["hbm_read_GBps"], 4)
+    if not args.no_gemm_scenarios:
+        line["grouped_gemm_scenarios"] = gemm_scenarios(args.steps, args.warmup, torch, moe, W)
     extra = [e for e in args.extra.split(",") if e]
     if extra:
         line["extra"] = {}

@@ -177,6 +177,60 @@ def moe_grouped_gemm(a: torch.Tensor, a_row_div: int, w: torch.Tensor,
     return c
 
 
+class IndexedGroupedGemm:
+    """The contiguous grouped GEMM of the axolotl page (``cg_grouped_gemm_forward``):
+    ``out[i] = x[i] @ w[expert_indices[i]].T`` for x bf16 [M, K], w bf16
+    [G, N, K] and int32 indices [M] (any grouping).  Two library calls:
+    ``moe_align`` over the indices as top-1 routing, then ``moe_grouped_gemm``
+    with the scatter epilogue and no weights.  The align outputs and the
+    workspace are allocated once here, so ``run()`` only launches."""
+
+    def __init__(self, x: torch.Tensor, w: torch.Tensor, expert_indices: torch.Tensor,
+                 block_m: int = 128, out: Optional[torch.Tensor] = None):
+        _dev(x, "x", torch.bfloat16)
+        _dev(w, "w", torch.bfloat16)
+        G, N, K = w.shape
+        M = x.shape[0]
+        if x.dim() != 2 or x.shape[1] != K:
+            raise ValueError("x must be [M, K] with the K of w")
+        _dev(expert_indices, "expert_indices", torch.int32, (M,))
+        if out is None:
+            out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+        _dev(out, "out", out.dtype, (M, N))
+        self.x, self.w, self.out, self.block_m = x, w, out, block_m
+        self.ids = expert_indices.view(M, 1)
+        self.G, self.M = G, M
+        cap = align_capacity(M, 1, G, block_m)
+        dev = x.device
+        self.sorted = torch.empty(cap, dtype=torch.int32, device=dev)
+        self.expert_ids = torch.empty(max(cap // block_m, 1), dtype=torch.int32, device=dev)
+        self.ntpp = torch.empty(1, dtype=torch.int32, device=dev)
+        n = ctypes.c_size_t(0)
+        _check("moe_align", lib().moe_align(_ptr(self.ids), M, 1, G, block_m, None, None, None,
+                                            cap, None, ctypes.byref(n), None))
+        self.workspace = _workspace(n.value, dev)
+
+    def align(self, stream=None):
+        moe_align(self.ids, self.G, self.block_m, self.sorted, self.expert_ids, self.ntpp,
+                  self.workspace, stream)
+
+    def gemm(self, stream=None) -> torch.Tensor:
+        return moe_grouped_gemm(self.x, 1, self.w, self.sorted, self.expert_ids, self.ntpp,
+                                self.block_m, self.M, EPI_WEIGHTED_SCATTER, self.out, None, stream)
+
+    def run(self, stream=None) -> torch.Tensor:
+        self.align(stream)
+        return self.gemm(stream)
+
+
+def indexed_grouped_gemm(x: torch.Tensor, w: torch.Tensor, expert_indices: torch.Tensor,
+                         block_m: int = 128, out: Optional[torch.Tensor] = None,
+                         stream=None) -> torch.Tensor:
+    """One-shot form of :class:`IndexedGroupedGemm`; returns ``out`` (bf16
+    [M, N] unless a float32 ``out`` is passed)."""
+    return IndexedGroupedGemm(x, w, expert_indices, block_m, out).run(stream)
+
+
 # ---------------------------------------------------------------- moe_fused_forward
 @dataclass
 class LayerParams:

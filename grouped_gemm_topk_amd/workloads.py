@@ -208,3 +208,76 @@ def small_config(name: str = "small", **kw) -> MoEConfig:
     base = dict(name=name, family=100, T=37, H=64, I=96, E=8, top_k=2, block_m=16)
     base.update(kw)
     return MoEConfig(**base)
+
+
+# ---------------------------------------------------------------------------
+# standalone grouped GEMM (rows mapped to experts by an index per row)
+# ---------------------------------------------------------------------------
+_TID_GX, _TID_GW, _TID_GPERM = 11, 12, 13
+
+
+@dataclasses.dataclass(frozen=True)
+class GemmScenario:
+    """One contiguous grouped GEMM: M rows of K, G expert matrices [N, K].
+
+    The four full-size scenarios are the table of the axolotl page's
+    ``benchmark_cg_gemm`` script (uniform groups of M / G rows, inputs and
+    weights drawn from N(0, 1) as that script's ``randn`` does).  ``sizes``
+    gives uneven (contiguous) groups instead; ``shuffled`` permutes the rows'
+    indices so that groups are not contiguous."""
+
+    name: str
+    family: int
+    G: int
+    M: int
+    N: int
+    K: int
+    sizes: Optional[tuple] = None
+    shuffled: bool = False
+    block_m: int = 128
+
+    def flops(self) -> float:
+        return 2.0 * self.M * self.N * self.K
+
+
+GEMM_SCENARIOS: Dict[str, GemmScenario] = {
+    s.name: s for s in (
+        GemmScenario("cg_g4_m8192_n4096_k7168", 6, G=4, M=8192, N=4096, K=7168),
+        GemmScenario("cg_g4_m8192_n7168_k2048", 6, G=4, M=8192, N=7168, K=2048),
+        GemmScenario("cg_g8_m4096_n4096_k7168", 6, G=8, M=4096, N=4096, K=7168),
+        GemmScenario("cg_g8_m4096_n7168_k2048", 6, G=8, M=4096, N=7168, K=2048),
+    )
+}
+
+
+def small_gemm_scenario(name: str = "cg_small", **kw) -> GemmScenario:
+    """A grouped-GEMM scenario for oracle-sized parity cases."""
+    base = dict(name=name, family=106, G=3, M=480, N=320, K=200)
+    base.update(kw)
+    return GemmScenario(**base)
+
+
+def make_gemm_inputs(sc: GemmScenario, threads: Optional[int] = None) -> Dict[str, np.ndarray]:
+    """``x`` (bf16 bits [M, K]), ``w`` (bf16 bits [G, N, K], one stream per
+    expert) and ``expert_indices`` (int32 [M])."""
+    if sc.sizes is not None:
+        sizes = np.asarray(sc.sizes, dtype=np.int64)
+        if sizes.size != sc.G or int(sizes.sum()) != sc.M:
+            raise ValueError("group sizes must be G entries summing to M")
+    else:
+        if sc.M % sc.G:
+            raise ValueError("uniform groups need M divisible by G")
+        sizes = np.full(sc.G, sc.M // sc.G, dtype=np.int64)
+    idx = np.repeat(np.arange(sc.G, dtype=np.int32), sizes)
+    if sc.shuffled:
+        idx = idx[_rng(sc.family, sc.M, _TID_GPERM).permutation(sc.M)]
+    w = np.empty((sc.G, sc.N, sc.K), dtype=np.uint16)
+
+    def fill(e: int) -> None:
+        w[e] = _normal_bf16((sc.N, sc.K), 1.0, sc.family, sc.M, _TID_GW, e)
+
+    nthreads = threads or min(16, len(os.sched_getaffinity(0)))
+    with ThreadPoolExecutor(max(1, nthreads)) as ex:
+        list(ex.map(fill, range(sc.G)))
+    return {"x": _normal_bf16((sc.M, sc.K), 1.0, sc.family, sc.M, _TID_GX),
+            "w": w, "expert_indices": np.ascontiguousarray(idx)}

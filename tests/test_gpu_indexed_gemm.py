@@ -1,0 +1,108 @@
+"""Parity of the indexed (contiguous) grouped GEMM against the oracle.
+
+out[i] = x[i] @ w[expert_indices[i]].T through moe_align (top-1) and
+moe_grouped_gemm (scatter by slot, weight 1).  Small cases are compared
+element by element; the four full-size scenarios of the axolotl page's
+benchmark table are run in the launch configuration the benchmark times and
+checked on sampled rows (first and last row of every group plus random ones),
+with every output row required to be written.
+"""
+import numpy as np
+import pytest
+
+from grouped_gemm_topk_amd import workloads as W
+from oracle import moe_oracle as O
+from tests.helpers import to_dev
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def moe():
+    from grouped_gemm_topk_amd import moe as M
+    M.lib()
+    return M
+
+
+def _tol(ref, fp32):
+    # bf16 output: one bf16 step of the value (round-to-nearest of an fp32
+    # result that may sit on the other side of a rounding boundary); fp32:
+    # accumulation-order differences over K
+    rel = 1e-5 if fp32 else 2.0 ** -8
+    return rel * np.abs(ref) + 1e-4 * np.abs(ref).max()
+
+
+SMALL = [
+    W.small_gemm_scenario("cg_uniform_pad"),                                   # 160-row groups, BM 128
+    W.small_gemm_scenario("cg_uneven_empty", sizes=(0, 200, 280)),
+    W.small_gemm_scenario("cg_shuffled", sizes=(100, 3, 377), shuffled=True),
+    W.small_gemm_scenario("cg_g8_bm64", G=8, M=8 * 70, N=136, K=264, block_m=64),
+    W.small_gemm_scenario("cg_g8_bm32", G=8, M=8 * 33, N=64, K=72, block_m=32),
+    W.small_gemm_scenario("cg_g5_bm16", G=5, M=5 * 21, N=520, K=48, block_m=16),
+    W.small_gemm_scenario("cg_g1", G=1, M=300, N=256, K=128),
+    W.small_gemm_scenario("cg_one_row", G=4, M=1, N=64, K=64, sizes=(0, 0, 1, 0)),
+]
+
+
+@pytest.mark.parametrize("sc", SMALL, ids=[s.name for s in SMALL])
+@pytest.mark.parametrize("fp32", [False, True], ids=["bf16", "fp32"])
+def test_indexed_grouped_gemm_small(moe, sc, fp32):
+    print(f"indexed grouped gemm {sc.name} fp32={fp32}", flush=True)
+    inp = W.make_gemm_inputs(sc)
+    ref = O.indexed_grouped_gemm(O.bf16_to_f64(inp["x"]), O.bf16_to_f64(inp["w"]),
+                                 inp["expert_indices"])
+    out = torch.full((sc.M, sc.N), float("nan"), device="cuda",
+                     dtype=torch.float32 if fp32 else torch.bfloat16)
+    moe.indexed_grouped_gemm(to_dev(inp["x"]), to_dev(inp["w"]), to_dev(inp["expert_indices"]),
+                             sc.block_m, out)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    assert np.all(np.isfinite(got)), "rows left unwritten"
+    bad = np.abs(got - ref) > _tol(ref, fp32)
+    assert not bad.any(), f"{bad.sum()} mismatches, worst {np.abs(got - ref).max()}"
+
+
+def test_indexed_grouped_gemm_reuse_and_new_indices(moe):
+    """The same object run twice, then with other indices written into its
+    index tensor: every run reflects the indices it saw."""
+    sc = W.small_gemm_scenario("cg_reuse", sizes=(50, 150, 280))
+    inp = W.make_gemm_inputs(sc)
+    xd, wd = to_dev(inp["x"]), to_dev(inp["w"])
+    idx = to_dev(inp["expert_indices"])
+    op = moe.IndexedGroupedGemm(xd, wd, idx, sc.block_m)
+    x64, w64 = O.bf16_to_f64(inp["x"]), O.bf16_to_f64(inp["w"])
+    for rep, new in enumerate([None, None, np.random.default_rng(3).integers(0, 3, sc.M)]):
+        if new is not None:
+            idx.copy_(torch.from_numpy(new.astype(np.int32)))
+            ids_np = new
+        else:
+            ids_np = inp["expert_indices"]
+        got = op.run().float().cpu().numpy()
+        ref = O.indexed_grouped_gemm(x64, w64, ids_np)
+        assert not (np.abs(got - ref) > _tol(ref, False)).any(), f"run {rep}"
+
+
+FULL = list(W.GEMM_SCENARIOS.values())
+
+
+@pytest.mark.parametrize("sc", FULL, ids=[s.name for s in FULL])
+def test_indexed_grouped_gemm_full_size_sampled(moe, sc):
+    print(f"indexed grouped gemm full size {sc.name}", flush=True)
+    inp = W.make_gemm_inputs(sc)
+    out = torch.full((sc.M, sc.N), float("nan"), device="cuda", dtype=torch.bfloat16)
+    op = moe.IndexedGroupedGemm(to_dev(inp["x"]), to_dev(inp["w"]), to_dev(inp["expert_indices"]),
+                                sc.block_m, out)
+    op.run()
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all()), "rows left unwritten"
+    idx = inp["expert_indices"]
+    starts = np.flatnonzero(np.r_[True, idx[1:] != idx[:-1]])
+    ends = np.r_[starts[1:], sc.M] - 1
+    rng = np.random.default_rng(11)
+    rows = np.unique(np.r_[starts, ends, rng.integers(0, sc.M, 24)])
+    ref = O.indexed_grouped_gemm(O.bf16_to_f64(inp["x"]), O.bf16_to_f64(inp["w"]), idx, rows=rows)
+    got = out[torch.from_numpy(rows).cuda()].float().cpu().numpy()
+    bad = np.abs(got - ref) > _tol(ref, False)
+    assert not bad.any(), f"{bad.sum()} mismatches, worst {np.abs(got - ref).max()}"
