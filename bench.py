@@ -47,8 +47,8 @@ DOMINANT_TRAFFIC = {
     "src": "grouped_gemm_topk_amd/csrc/gemm.hip",
     "sha256": "0154cf8966bf34e05af79856beda3a2c23b0a0cda574295a156130c29f5c7790",
     "config": "dsv3",
-    "fetch_bytes": 1298403123,
-    "write_bytes": 89789132,
+    "fetch_bytes": 1303026892,
+    "write_bytes": 89790156,
 }
 
 
@@ -65,6 +65,8 @@ def parse():
     ap.add_argument("--no-peaks", action="store_true", help="skip the achievable-peak probes")
     ap.add_argument("--no-gemm-scenarios", action="store_true",
                     help="skip the standalone grouped-GEMM scenarios")
+    ap.add_argument("--gemm-scenarios-only", action="store_true",
+                    help="only the standalone grouped-GEMM scenarios (one JSON line), for profiler passes")
     ap.add_argument("--cpu-tokens", type=int, default=4096,
                     help="tokens of the workload the CPU oracle runs on")
     ap.add_argument("--extra", default="", help="comma list of more configs to time (report only)")
@@ -296,19 +298,31 @@ def _event_ms(fn, steps, warmup, torch):
     return e0.elapsed_time(e1) / steps
 
 
+def _interleaved_ms(fns, steps, warmup, torch, rounds=5):
+    """Median ms per call of each function, timed in alternation over several
+    rounds (the order within a run otherwise favours whichever comes later)."""
+    for f in fns:
+        for _ in range(warmup):
+            f()
+    times = [[] for _ in fns]
+    for _ in range(rounds):
+        for i, f in enumerate(fns):
+            times[i].append(_event_ms(f, steps, 1, torch))
+    return [float(np.median(t)) for t in times]
+
+
 def gemm_scenarios(steps, warmup, torch, moe, W):
     """The contiguous grouped GEMM at the four shapes of the axolotl page's
     benchmark table (uniform groups): the whole call (align of the per-row
     indices + grouped GEMM) and the GEMM launch alone, plus hipBLASLt (one
-    torch.matmul per group on a contiguous transposed weight) as context."""
+    torch.matmul per group on a contiguous transposed weight) as context.
+    The three are timed in alternation over five rounds; medians."""
     res = []
     for sc in W.GEMM_SCENARIOS.values():
         inp = W.make_gemm_inputs(sc)
         x, w = _to_dev(inp["x"], torch), _to_dev(inp["w"], torch)
         op = moe.IndexedGroupedGemm(x, w, _to_dev(inp["expert_indices"], torch), sc.block_m)
         op.run()
-        ms_call = _event_ms(op.run, steps, warmup, torch)
-        ms_gemm = _event_ms(op.gemm, steps, warmup, torch)
         gsz = sc.M // sc.G
         wt = [w[g].t().contiguous() for g in range(sc.G)]
         xs = [x[g * gsz:(g + 1) * gsz] for g in range(sc.G)]
@@ -318,7 +332,7 @@ def gemm_scenarios(steps, warmup, torch, moe, W):
         def blas():
             for g in range(sc.G):
                 torch.matmul(xs[g], wt[g], out=outs[g])
-        ms_blas = _event_ms(blas, steps, warmup, torch)
+        ms_call, ms_gemm, ms_blas = _interleaved_ms([op.run, op.gemm, blas], steps, warmup, torch)
         f = sc.flops()
         res.append({"scenario": sc.name, "G": sc.G, "M": sc.M, "N": sc.N, "K": sc.K,
                     "block_m": sc.block_m, "ms": round(ms_call, 4),
@@ -450,6 +464,10 @@ def main():
         copy_calibration(torch)
         return
     moe.lib()
+    if args.gemm_scenarios_only:
+        print(json.dumps({"grouped_gemm_scenarios": gemm_scenarios(args.steps, args.warmup, torch,
+                                                                   moe, W)}), flush=True)
+        return
     if args.decode_only:
         print(json.dumps({"decode": [decode_case(n, torch, moe, W, O) for n in DECODE_CASES]}),
               flush=True)

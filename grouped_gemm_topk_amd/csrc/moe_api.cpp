@@ -43,12 +43,17 @@ bool valid_bm(int bm) { return bm == 16 || bm == 32 || bm == 64 || bm == 128; }
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-int align_nblocks(int64_t n) { return (int)((n + moe::kAlignChunk - 1) / moe::kAlignChunk); }
+// chunks of the two-kernel align: at least kAlignMinChunk slots each, at most
+// kAlignMaxChunks of them
+int align_nblocks(int64_t n) {
+  const int64_t nb = (n + moe::kAlignMinChunk - 1) / moe::kAlignMinChunk;
+  return (int)(nb < moe::kAlignMaxChunks ? nb : moe::kAlignMaxChunks);
+}
 
-// scratch of the multi-block align: per-chunk histograms + expert offsets
+// scratch of the two-kernel align: one expert histogram per chunk
 size_t align_scratch_bytes(int64_t n, int E) {
   if (n <= moe::kSingleBlockSlots) return 0;
-  return round_up((size_t)(align_nblocks(n) + 1) * E * sizeof(int), 256);
+  return round_up((size_t)align_nblocks(n) * E * sizeof(int), 256);
 }
 
 // Carves a workspace into 256-byte aligned regions.
@@ -132,8 +137,8 @@ moe::AlignParams make_align(const int32_t* ids, int64_t n, int E, int bm, int32_
   a.expert_ids = expert_ids;
   a.ntpp = ntpp;
   a.nblocks = align_nblocks(n);
+  a.chunk = a.nblocks > 0 ? (int)((n + a.nblocks - 1) / a.nblocks) : 0;
   a.block_counts = scratch;
-  a.expert_off = scratch ? scratch + (int64_t)a.nblocks * E : nullptr;
   return a;
 }
 

@@ -31,13 +31,14 @@ struct AlignParams {
   int* sorted_ids;      // [capacity]
   int* expert_ids;      // [capacity / block_m]
   int* ntpp;            // [1]
-  int* block_counts;    // workspace [nblocks, E] (multi-block path)
-  int* expert_off;      // workspace [E]          (multi-block path)
-  int nblocks;          // chunks of kAlignChunk slots
+  int* block_counts;    // workspace [nblocks, E] (two-kernel path)
+  int nblocks;          // chunks (workgroups) of the two-kernel path
+  int chunk;            // slots per chunk
 };
 
-constexpr int kAlignChunk = 4096;      // slots per workgroup in the multi-block path
-constexpr int kSingleBlockSlots = 4096; // at most this many slots: one workgroup does it all
+constexpr int kAlignMinChunk = 1024;    // slots per workgroup of the two-kernel path, at least
+constexpr int kAlignMaxChunks = 64;     // workgroups of the two-kernel path, at most
+constexpr int kSingleBlockSlots = 1024; // at most this many slots: one workgroup does it all
 constexpr int kRouteFusedTokens = 64;   // gating fused into the one-workgroup align up to this T
 
 // ---------------------------------------------------------------- grouped GEMM

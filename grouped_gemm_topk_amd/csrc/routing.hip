@@ -149,112 +149,126 @@ __device__ void gate_token(const GateParams& p, int t, double* s_sig, int* s_kee
 }
 
 // ------------------------------------------------------------------ align helpers
-// Exclusive scan of the padded expert sizes by wave 0 of the block.  Fills
-// s_off[e] (start) and returns nothing; s_cnt holds the counts.  Then writes
-// expert_ids, the pads and num_tokens_post_padded.
-__device__ void align_layout(const int* s_cnt, int* s_off, int* s_cursor, int E, int bm, int n,
-                             int* sorted_ids, int* expert_ids, int* ntpp, int* s_total) {
+// Padded exclusive scan of the expert counts by wave 0 (four experts per
+// lane): s_off[e] = start of expert e in the padded order, *s_total = padded
+// length.  The caller synchronises before reading them.
+__device__ void align_offsets(const int* s_cnt, int* s_off, int E, int bm, int* s_total) {
   const int tid = threadIdx.x;
-  if (tid < kWave) {
-    // each lane owns 4 consecutive experts
-    int base = tid * 4;
-    int pc[4];
-    int local = 0;
+  if (tid >= kWave) return;
+  const int base = tid * 4;
+  int pc[4];
+  int local = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int e = base + i;
-      int c = e < E ? s_cnt[e] : 0;
-      pc[i] = (c + bm - 1) / bm * bm;
-      local += pc[i];
-    }
-    int incl = local;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      int o = __shfl_up(incl, off, kWave);
-      if (tid >= off) incl += o;
-    }
-    int run = incl - local;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int e = base + i;
-      if (e < E) { s_off[e] = run; s_cursor[e] = run; }
-      run += pc[i];
-    }
-    if (tid == kWave - 1) {
-      *s_total = incl;
-      *ntpp = incl;
-    }
+  for (int i = 0; i < 4; ++i) {
+    const int e = base + i;
+    const int c = e < E ? s_cnt[e] : 0;
+    pc[i] = (c + bm - 1) / bm * bm;   // an empty expert takes no block
+    local += pc[i];
   }
-  __syncthreads();
-  const int total = *s_total;
-  // expert of every block: the last expert whose offset is <= block start
+  int incl = local;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int o = __shfl_up(incl, off, kWave);
+    if (tid >= off) incl += o;
+  }
+  int run = incl - local;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = base + i;
+    if (e < E) s_off[e] = run;
+    run += pc[i];
+  }
+  if (tid == kWave - 1) *s_total = incl;
+}
+
+// expert_ids of every block, the pad entries of sorted_ids (value n) and the
+// padded total, all threads of the workgroup in parallel.
+__device__ void write_layout(const int* s_cnt, const int* s_off, int E, int bm, int n, int total,
+                             int* sorted_ids, int* expert_ids, int* ntpp) {
+  const int tid = threadIdx.x;
+  if (tid == 0) *ntpp = total;
+  // expert of a block: the last expert whose offset is <= the block start (an
+  // empty expert shares its offset with the next one, so the last such expert
+  // is the non-empty one that owns the block)
   for (int b = tid; b * bm < total; b += blockDim.x) {
-    int pos = b * bm;
+    const int pos = b * bm;
     int lo = 0, hi = E - 1;
     while (lo < hi) {
-      int mid = (lo + hi + 1) >> 1;
+      const int mid = (lo + hi + 1) >> 1;
       if (s_off[mid] <= pos) lo = mid; else hi = mid - 1;
     }
-    // skip empty experts that share the offset: take the first non-empty one at pos
-    // (an empty expert has the same offset as the next one; the binary search
-    // returned the last e with off <= pos, which is non-empty because pos < total)
     expert_ids[b] = lo;
   }
-  // pads of each expert
-  for (int e = tid; e < E; e += blockDim.x) {
-    int c = s_cnt[e];
-    int pcount = (c + bm - 1) / bm * bm;
-    for (int r = c; r < pcount; ++r) sorted_ids[s_off[e] + r] = n;
+  // pads: expert e owns padded positions [off + c, off + round_up(c, bm))
+  for (int idx = tid; idx < E * bm; idx += blockDim.x) {
+    const int e = idx / bm, r = idx - e * bm;
+    const int c = s_cnt[e];
+    const int pc = (c + bm - 1) / bm * bm;
+    if (c + r < pc) sorted_ids[s_off[e] + c + r] = n;
   }
 }
 
+// Lanes of this wave whose expert equals e (one ballot per bit of the id);
+// lanes with e < 0 are excluded.
+__device__ __forceinline__ uint64_t same_expert(int e, int nbits) {
+  uint64_t match = __ballot(e >= 0);
+  for (int b = 0; b < nbits; ++b) {
+    const uint64_t bal = __ballot(e >= 0 && ((e >> b) & 1));
+    match &= ((e >> b) & 1) ? bal : ~bal;
+  }
+  return e >= 0 ? match : 0ull;
+}
+
+__device__ __forceinline__ int id_bits(int E) {
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  return nbits;
+}
+
 // Stable scatter of `cnt` slots starting at `slot0`, whose experts are read by
-// `get_id(i)` (i in [0, cnt)).  s_cursor[e] holds the next write position of
-// expert e and is advanced.  s_wcnt is LDS scratch [2][16][MOE_MAX_EXPERTS].
+// `get_id(i)` (i in [0, cnt)), by a 1024-thread workgroup.  s_cursor[e] holds
+// the next write position of expert e and is advanced.  LDS scratch: s_wcnt
+// and s_base, [16 waves][256 experts] each; s_wcnt must be zero on entry and
+// is left zero.
 template <typename GetId>
 __device__ void stable_scatter(GetId get_id, int slot0, int cnt, int E, int* s_cursor,
-                               int* s_wcnt, int* sorted_ids) {
+                               int* s_wcnt, int* s_base, int* sorted_ids) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
-  const int nwaves = blockDim.x / kWave;
-  int nbits = 0;
-  while ((1 << nbits) < E) ++nbits;
+  const int nbits = id_bits(E);
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
-  // clear both buffers
-  for (int i = tid; i < 2 * 16 * 256; i += blockDim.x) s_wcnt[i] = 0;
-  __syncthreads();
-  int it = 0;
-  for (int base = 0; base < cnt; base += blockDim.x, ++it) {
-    int* buf = s_wcnt + (it & 1) * (16 * 256);
-    int* other = s_wcnt + ((it + 1) & 1) * (16 * 256);
-    int i = base + tid;
+  for (int base = 0; base < cnt; base += 1024) {
+    const int i = base + tid;
     int e = -1;
     if (i < cnt) {
       e = get_id(i);
       if (e < 0 || e >= E) e = -1;
     }
-    uint64_t match = __ballot(e >= 0);
-    for (int b = 0; b < nbits; ++b) {
-      uint64_t bal = __ballot(e >= 0 && ((e >> b) & 1));
-      match &= ((e >> b) & 1) ? bal : ~bal;
-    }
-    int rank = __popcll(match & lt_mask);
-    if (e >= 0 && rank == 0) buf[wave * 256 + e] = __popcll(match);
+    const uint64_t match = same_expert(e, nbits);
+    const int rank = __popcll(match & lt_mask);
+    if (e >= 0 && rank == 0) s_wcnt[wave * 256 + e] = __popcll(match);
     __syncthreads();
-    // per-expert exclusive prefix over the waves, plus the running cursor
-    for (int x = tid; x < E; x += blockDim.x) {
-      int run = s_cursor[x];
-      for (int w = 0; w < nwaves; ++w) {
-        int c = buf[w * 256 + x];
-        buf[w * 256 + x] = run;
-        run += c;
-        other[w * 256 + x] = 0;
+    // per expert: exclusive prefix over the 16 waves (16 lanes per expert, a
+    // width-16 shuffle scan), plus the running cursor; counts are cleared
+    for (int e0 = wave * 4; e0 < E; e0 += 64) {
+      const int ee = e0 + (lane >> 4), ww = lane & 15;
+      const int v = ee < E ? s_wcnt[ww * 256 + ee] : 0;
+      int incl = v;
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) {
+        const int o = __shfl_up(incl, off, 16);
+        if (ww >= off) incl += o;
       }
-      s_cursor[x] = run;
+      if (ee < E) {
+        const int cur = s_cursor[ee];
+        s_base[ww * 256 + ee] = cur + incl - v;
+        s_wcnt[ww * 256 + ee] = 0;
+        if (ww == 15) s_cursor[ee] = cur + incl;
+      }
     }
     __syncthreads();
-    if (e >= 0) sorted_ids[buf[wave * 256 + e] + rank] = slot0 + i;
+    if (e >= 0) sorted_ids[s_base[wave * 256 + e] + rank] = slot0 + i;
   }
 }
 
@@ -275,13 +289,13 @@ __global__ void __launch_bounds__(256) gate_kernel(GateParams p) {
   }
 }
 
-// One workgroup: all n <= kSingleBlockSlots slots.  When `g` is given, gating
-// runs first inside the same workgroup (one wave per token).
+// One workgroup: all n <= kSingleBlockSlots slots.  When `do_gate` is set,
+// gating runs first inside the same workgroup (one wave per token).
 __global__ void __launch_bounds__(1024) align_single_kernel(AlignParams a, GateParams g,
                                                             int do_gate) {
   __shared__ int s_ids[kSingleBlockSlots];
   __shared__ int s_cnt[256], s_off[256], s_cursor[256];
-  __shared__ int s_wcnt[2 * 16 * 256];
+  __shared__ int s_wcnt[16 * 256], s_base[16 * 256];
   __shared__ int s_total;
   __shared__ double s_sig[16][256];
   __shared__ int s_keep[16][64];
@@ -304,67 +318,86 @@ __global__ void __launch_bounds__(1024) align_single_kernel(AlignParams a, GateP
     for (int i = tid; i < a.n; i += blockDim.x) s_ids[i] = a.topk_ids[i];
   }
   for (int e = tid; e < 256; e += blockDim.x) s_cnt[e] = 0;
+  for (int i = tid; i < 16 * 256; i += blockDim.x) s_wcnt[i] = 0;
   __syncthreads();
   for (int i = tid; i < a.n; i += blockDim.x) {
-    int e = s_ids[i];
+    const int e = s_ids[i];
     if (e >= 0 && e < a.E) atomicAdd(&s_cnt[e], 1);
   }
   __syncthreads();
-  align_layout(s_cnt, s_off, s_cursor, a.E, a.block_m, a.n, a.sorted_ids, a.expert_ids, a.ntpp,
-               &s_total);
+  align_offsets(s_cnt, s_off, a.E, a.block_m, &s_total);
   __syncthreads();
-  stable_scatter([&](int i) { return s_ids[i]; }, 0, a.n, a.E, s_cursor, s_wcnt, a.sorted_ids);
+  write_layout(s_cnt, s_off, a.E, a.block_m, a.n, s_total, a.sorted_ids, a.expert_ids, a.ntpp);
+  for (int e = tid; e < a.E; e += blockDim.x) s_cursor[e] = s_off[e];
+  __syncthreads();
+  stable_scatter([&](int i) { return s_ids[i]; }, 0, a.n, a.E, s_cursor, s_wcnt, s_base,
+                 a.sorted_ids);
 }
 
-// Multi-block path, step 1: per-chunk expert histogram.
+// Two-kernel path, step 1: expert histogram of each chunk of a.chunk slots
+// (one leader per expert and wave adds the wave's count).
 __global__ void __launch_bounds__(1024) align_count_kernel(AlignParams a) {
   __shared__ int s_cnt[256];
   const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  const int nbits = id_bits(a.E);
   for (int e = tid; e < 256; e += blockDim.x) s_cnt[e] = 0;
   __syncthreads();
-  const int s0 = blockIdx.x * kAlignChunk;
-  const int s1 = min(a.n, s0 + kAlignChunk);
-  for (int s = s0 + tid; s < s1; s += blockDim.x) {
-    int e = a.topk_ids[s];
-    if (e >= 0 && e < a.E) atomicAdd(&s_cnt[e], 1);
+  const int64_t s0 = (int64_t)blockIdx.x * a.chunk;
+  const int64_t s1 = min((int64_t)a.n, s0 + a.chunk);
+  for (int64_t base = s0; base < s1; base += 1024) {
+    const int64_t s = base + tid;
+    int e = s < s1 ? a.topk_ids[s] : -1;
+    if (e >= a.E) e = -1;
+    const uint64_t match = same_expert(e, nbits);
+    if (e >= 0 && __popcll(match & lt_mask) == 0) atomicAdd(&s_cnt[e], __popcll(match));
   }
   __syncthreads();
   for (int e = tid; e < a.E; e += blockDim.x) a.block_counts[blockIdx.x * a.E + e] = s_cnt[e];
 }
 
-// Step 2: one workgroup turns chunk histograms into per-chunk bases, pads the
-// experts and writes expert_ids and the padded total.
-__global__ void __launch_bounds__(1024) align_scan_kernel(AlignParams a) {
+// Step 2: every workgroup derives the expert offsets and its chunk's base per
+// expert from all chunk histograms (a few KB from L2), workgroup 0 writes the
+// layout (expert_ids, pads, padded total), and each workgroup scatters its
+// chunk's slots stably.
+__global__ void __launch_bounds__(1024) align_place_kernel(AlignParams a) {
+  __shared__ int s_tot[4][256], s_pre[4][256];
   __shared__ int s_cnt[256], s_off[256], s_cursor[256];
+  __shared__ int s_wcnt[16 * 256], s_base[16 * 256];
   __shared__ int s_total;
   const int tid = threadIdx.x;
-  for (int e = tid; e < a.E; e += blockDim.x) {
-    int run = 0;
-    for (int b = 0; b < a.nblocks; ++b) {
-      int c = a.block_counts[b * a.E + e];
-      a.block_counts[b * a.E + e] = run;
-      run += c;
+  const int q = tid >> 8, e = tid & 255;
+  for (int i = tid; i < 16 * 256; i += blockDim.x) s_wcnt[i] = 0;
+  {
+    int tot = 0, pre = 0;
+    if (e < a.E) {
+      for (int b = q; b < a.nblocks; b += 4) {
+        const int c = a.block_counts[b * a.E + e];
+        tot += c;
+        if (b < (int)blockIdx.x) pre += c;
+      }
     }
-    s_cnt[e] = run;
+    s_tot[q][e] = tot;
+    s_pre[q][e] = pre;
   }
   __syncthreads();
-  align_layout(s_cnt, s_off, s_cursor, a.E, a.block_m, a.n, a.sorted_ids, a.expert_ids, a.ntpp,
-               &s_total);
-  for (int e = tid; e < a.E; e += blockDim.x) a.expert_off[e] = s_off[e];
-}
-
-// Step 3: each chunk scatters its slots at expert offset + chunk base.
-__global__ void __launch_bounds__(1024) align_scatter_kernel(AlignParams a) {
-  __shared__ int s_cursor[256];
-  __shared__ int s_wcnt[2 * 16 * 256];
-  const int tid = threadIdx.x;
-  for (int e = tid; e < a.E; e += blockDim.x)
-    s_cursor[e] = a.expert_off[e] + a.block_counts[blockIdx.x * a.E + e];
+  if (tid < 256) {
+    s_cnt[tid] = s_tot[0][tid] + s_tot[1][tid] + s_tot[2][tid] + s_tot[3][tid];
+    s_pre[0][tid] += s_pre[1][tid] + s_pre[2][tid] + s_pre[3][tid];
+  }
   __syncthreads();
-  const int s0 = blockIdx.x * kAlignChunk;
-  const int cnt = min(a.n, s0 + kAlignChunk) - s0;
+  align_offsets(s_cnt, s_off, a.E, a.block_m, &s_total);
+  __syncthreads();
+  if (blockIdx.x == 0)
+    write_layout(s_cnt, s_off, a.E, a.block_m, a.n, s_total, a.sorted_ids, a.expert_ids, a.ntpp);
+  for (int x = tid; x < a.E; x += blockDim.x) s_cursor[x] = s_off[x] + s_pre[0][x];
+  __syncthreads();
+  const int64_t s0 = (int64_t)blockIdx.x * a.chunk;
+  const int cnt = (int)(min((int64_t)a.n, s0 + a.chunk) - s0);
   const int* ids = a.topk_ids + s0;
-  stable_scatter([&](int i) { return ids[i]; }, s0, cnt, a.E, s_cursor, s_wcnt, a.sorted_ids);
+  stable_scatter([&](int i) { return ids[i]; }, (int)s0, cnt, a.E, s_cursor, s_wcnt, s_base,
+                 a.sorted_ids);
 }
 
 }  // namespace
@@ -388,8 +421,7 @@ hipError_t launch_align(const AlignParams& p, hipStream_t s) {
     return hipGetLastError();
   }
   hipLaunchKernelGGL(align_count_kernel, dim3(p.nblocks), dim3(1024), 0, s, p);
-  hipLaunchKernelGGL(align_scan_kernel, dim3(1), dim3(1024), 0, s, p);
-  hipLaunchKernelGGL(align_scatter_kernel, dim3(p.nblocks), dim3(1024), 0, s, p);
+  hipLaunchKernelGGL(align_place_kernel, dim3(p.nblocks), dim3(1024), 0, s, p);
   return hipGetLastError();
 }
 

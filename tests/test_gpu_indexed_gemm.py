@@ -106,3 +106,31 @@ def test_indexed_grouped_gemm_full_size_sampled(moe, sc):
     got = out[torch.from_numpy(rows).cuda()].float().cpu().numpy()
     bad = np.abs(got - ref) > _tol(ref, False)
     assert not bad.any(), f"{bad.sum()} mismatches, worst {np.abs(got - ref).max()}"
+
+
+def test_indexed_grouped_gemm_graph_replays(moe):
+    """Captured once (align + GEMM) and replayed with eager work in between:
+    every replay equals the eager result bit for bit."""
+    sc = W.small_gemm_scenario("cg_graph", G=6, M=6 * 300, N=384, K=256, sizes=(0, 700, 300, 1, 499, 300))
+    inp = W.make_gemm_inputs(sc)
+    op = moe.IndexedGroupedGemm(to_dev(inp["x"]), to_dev(inp["w"]), to_dev(inp["expert_indices"]),
+                                sc.block_m)
+    eager = op.run().clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        op.run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        out = op.run()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        op.out.fill_(float("nan"))
+        op.sorted.fill_(-7)
+        if rep == 1:
+            op.run()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {rep}"

@@ -55,6 +55,10 @@ def _run_fused(moe, cfg, inp, block_m=None):
     (100, 4, 18, "rand"), (513, 6, 128, "rand"), (700, 8, 256, "rand"),
     (4096, 4, 18, "rand"), (8192, 8, 128, "zipf"), (5000, 1, 1, "rand"), (1023, 5, 64, "one"),
     (0, 4, 8, "rand"), (2049, 2, 8, "rand"),
+    # the one-workgroup / two-kernel boundary (1024 slots), all slots on one
+    # expert past it, and more than 64 x 1024 slots (chunks of several passes)
+    (1024, 1, 4, "rand"), (1025, 1, 4, "rand"), (129, 8, 16, "one"),
+    (20000, 8, 256, "rand"), (9000, 8, 64, "zipf"),
 ])
 def test_align_bit_exact(moe, T, k, E, mode, bm):
     print(f"align T={T} k={k} E={E} mode={mode} bm={bm}", flush=True)
