@@ -19,7 +19,8 @@ Steps, in the order the skill card's *Token-Expert Routing* lists them:
 
 plus ``grouped_gemm`` (one grouped GEMM over the aligned layout),
 ``indexed_grouped_gemm`` (the standalone contiguous grouped GEMM of the
-axolotl page, rows mapped to experts by an index per row) and
+axolotl page, rows mapped to experts by an index per row),
+``indexed_grouped_gemm_backward`` (its input and weight gradients) and
 ``moe_forward`` (the whole layer).
 
 Readings where the pages are silent (each is pinned by a test unless marked):
@@ -345,6 +346,32 @@ def indexed_grouped_gemm(x: np.ndarray, w: np.ndarray, expert_indices: np.ndarra
         if sel.size:
             out[sel] = x[sel] @ w[e].T
     return out
+
+
+def indexed_grouped_gemm_backward(x: np.ndarray, w: np.ndarray, expert_indices: np.ndarray,
+                                  dy: np.ndarray):
+    """Gradients of the indexed grouped GEMM ``out[i] = x[i] @ w[idx[i]].T``
+    for an output gradient ``dy`` (the axolotl page's ``cg_backward.py``:
+    ``cg_grouped_gemm_backward_inputs`` and ``..._weights``):
+
+        dx[i] = dy[i] @ w[idx[i]]                       ([M, K])
+        dw[e] = sum over rows i with idx[i] == e of outer(dy[i], x[i])
+              = dy[rows_e].T @ x[rows_e]                ([E, N, K]; zero if no rows)
+
+    Read per row, like the forward.  One matmul per expert, float64."""
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    dy = np.asarray(dy, dtype=np.float64)
+    idx = np.asarray(expert_indices).reshape(-1)
+    E, N, K = w.shape
+    dx = np.full((x.shape[0], K), np.nan)
+    dw = np.zeros((E, N, K))
+    for e in range(E):
+        sel = np.nonzero(idx == e)[0]
+        if sel.size:
+            dx[sel] = dy[sel] @ w[e]
+            dw[e] = dy[sel].T @ x[sel]
+    return dx, dw
 
 
 # ----------------------------------------------------------------------------

@@ -447,3 +447,54 @@ def test_indexed_grouped_gemm_equals_aligned_scatter():
     via = O.grouped_gemm(x, 1, w, al["sorted_token_ids"], al["expert_ids"],
                          al["num_tokens_post_padded"], bm, M, O.EPI_WEIGHTED_SCATTER, None)
     np.testing.assert_allclose(via, O.indexed_grouped_gemm(x, w, idx), rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------- its backward
+def test_indexed_backward_bruteforce():
+    """dx and dw element by element as pure-Python sums."""
+    rng = np.random.default_rng(15)
+    M, K, N, E = 6, 4, 3, 4
+    x, w, dy = rng.standard_normal((M, K)), rng.standard_normal((E, N, K)), rng.standard_normal((M, N))
+    idx = np.array([1, 1, 3, 0, 3, 3])            # expert 2 has no rows
+    dx, dw = O.indexed_grouped_gemm_backward(x, w, idx, dy)
+    for i in range(M):
+        for k in range(K):
+            s = sum(float(dy[i, n]) * float(w[idx[i], n, k]) for n in range(N))
+            assert abs(dx[i, k] - s) <= 1e-12 * max(1.0, abs(s))
+    for e in range(E):
+        for n in range(N):
+            for k in range(K):
+                s = sum(float(dy[i, n]) * float(x[i, k]) for i in range(M) if idx[i] == e)
+                assert abs(dw[e, n, k] - s) <= 1e-12 * max(1.0, abs(s))
+    assert np.all(dw[2] == 0.0)
+
+
+def test_indexed_backward_adjoint_identities():
+    """The gradients are the adjoints of the forward: for any directions hx,
+    hw, <dy, F(hx, w)> = <dx, hx> and <dy, F(x, hw)> = <dw, hw> (F bilinear),
+    with F the pinned forward."""
+    rng = np.random.default_rng(16)
+    M, K, N, E = 40, 12, 9, 5
+    x, w, dy = rng.standard_normal((M, K)), rng.standard_normal((E, N, K)), rng.standard_normal((M, N))
+    idx = rng.integers(0, E, M)
+    dx, dw = O.indexed_grouped_gemm_backward(x, w, idx, dy)
+    hx, hw = rng.standard_normal((M, K)), rng.standard_normal((E, N, K))
+    lhs_x = float(np.sum(dy * O.indexed_grouped_gemm(hx, w, idx)))
+    lhs_w = float(np.sum(dy * O.indexed_grouped_gemm(x, hw, idx)))
+    assert abs(lhs_x - float(np.sum(dx * hx))) <= 1e-10 * abs(lhs_x)
+    assert abs(lhs_w - float(np.sum(dw * hw))) <= 1e-10 * abs(lhs_w)
+
+
+def test_indexed_backward_matches_autograd():
+    """torch.autograd (CPU, float64) of the per-row forward."""
+    rng = np.random.default_rng(17)
+    M, K, N, E = 30, 8, 10, 4
+    x, w, dy = rng.standard_normal((M, K)), rng.standard_normal((E, N, K)), rng.standard_normal((M, N))
+    idx = rng.integers(0, E, M)
+    xt = torch.tensor(x, requires_grad=True)
+    wt = torch.tensor(w, requires_grad=True)
+    out = torch.einsum("mk,mnk->mn", xt, wt[torch.from_numpy(idx)])
+    out.backward(torch.tensor(dy))
+    dx, dw = O.indexed_grouped_gemm_backward(x, w, idx, dy)
+    np.testing.assert_allclose(dx, xt.grad.numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(dw, wt.grad.numpy(), rtol=1e-12, atol=1e-12)
