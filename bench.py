@@ -315,8 +315,9 @@ def gemm_scenarios(steps, warmup, torch, moe, W):
     """The contiguous grouped GEMM at the four shapes of the axolotl page's
     benchmark table (uniform groups): the whole call (align of the per-row
     indices + grouped GEMM) and the GEMM launch alone, plus hipBLASLt (one
-    torch.matmul per group on a contiguous transposed weight) as context.
-    The three are timed in alternation over five rounds; medians."""
+    torch.matmul per group on a contiguous transposed weight) as context; then
+    the backward (input and weight gradients, each with its layout kernels)
+    beside hipBLASLt per group.  Timed in alternation over five rounds; medians."""
     res = []
     for sc in W.GEMM_SCENARIOS.values():
         inp = W.make_gemm_inputs(sc)
@@ -333,6 +334,28 @@ def gemm_scenarios(steps, warmup, torch, moe, W):
             for g in range(sc.G):
                 torch.matmul(xs[g], wt[g], out=outs[g])
         ms_call, ms_gemm, ms_blas = _interleaved_ms([op.run, op.gemm, blas], steps, warmup, torch)
+        # backward: dx (weight transpose + grouped GEMM) and dw (segment table,
+        # gathered transposes of dy and x + segmented GEMM), each 2 M N K flops
+        dy = _to_dev(W.make_gemm_inputs(sc, with_grad=True)["dy"], torch)
+        dxb = torch.empty((sc.M, sc.K), dtype=torch.bfloat16, device="cuda")
+        dwb = torch.empty((sc.G, sc.N, sc.K), dtype=torch.bfloat16, device="cuda")
+        op.backward(dy, dxb, dwb)
+        bdx = lambda: op.backward(dy, dxb, None, want_dw=False)
+        bdw = lambda: op.backward(dy, None, dwb, want_dx=False)
+        dys = [dy[g * gsz:(g + 1) * gsz] for g in range(sc.G)]
+        dyt = [d.t().contiguous() for d in dys]
+        ref_dx = torch.empty((sc.M, sc.K), dtype=torch.bfloat16, device="cuda")
+        ref_dw = torch.empty((sc.G, sc.N, sc.K), dtype=torch.bfloat16, device="cuda")
+
+        def blas_dx():
+            for g in range(sc.G):
+                torch.matmul(dys[g], w[g], out=ref_dx[g * gsz:(g + 1) * gsz])
+
+        def blas_dw():
+            for g in range(sc.G):
+                torch.matmul(dyt[g], xs[g], out=ref_dw[g])
+        ms_bdx, ms_bdw, ms_rdx, ms_rdw = _interleaved_ms([bdx, bdw, blas_dx, blas_dw], steps, warmup,
+                                                         torch)
         f = sc.flops()
         res.append({"scenario": sc.name, "G": sc.G, "M": sc.M, "N": sc.N, "K": sc.K,
                     "block_m": sc.block_m, "ms": round(ms_call, 4),
@@ -341,8 +364,13 @@ def gemm_scenarios(steps, warmup, torch, moe, W):
                     "gemm_TFLOPS": round(f / (ms_gemm * 1e-3) / 1e12, 1),
                     "mfma_frac": round(f / (ms_gemm * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
                     "hipblaslt_per_group_ms": round(ms_blas, 4),
-                    "hipblaslt_per_group_TFLOPS": round(f / (ms_blas * 1e-3) / 1e12, 1)})
-        del op, x, w, wt, xs, outs, ref_out
+                    "hipblaslt_per_group_TFLOPS": round(f / (ms_blas * 1e-3) / 1e12, 1),
+                    "backward": {
+                        "dx_ms": round(ms_bdx, 4), "dx_TFLOPS": round(f / (ms_bdx * 1e-3) / 1e12, 1),
+                        "dw_ms": round(ms_bdw, 4), "dw_TFLOPS": round(f / (ms_bdw * 1e-3) / 1e12, 1),
+                        "hipblaslt_per_group_dx_ms": round(ms_rdx, 4),
+                        "hipblaslt_per_group_dw_ms": round(ms_rdw, 4)}})
+        del op, x, w, wt, xs, outs, ref_out, dy, dxb, dwb, dys, dyt, ref_dx, ref_dw
         torch.cuda.empty_cache()
     return res
 

@@ -168,44 +168,64 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) grouped_gemm_ker
   // run of m-blocks are consecutive, in chunks of GM m-blocks with the n-tile
   // outer, so that neighbouring workgroups share weight tiles and token rows
   const int ntn = pin.ntiles_n;
-  const int tg = xcd_tile(blockIdx.x, ntn * (pin.mblocks + pin.nsb));
-  // tiles past the routed ones belong to the dense second part
-  const bool second = tg >= ntn * pin.mblocks;
   GemmParams p = pin;
-  if (second) {
-    p.A = pin.A2;
-    p.W = pin.W2;
-    p.E = 1;
-    p.a_row_div = 0;
-    p.sorted_ids = nullptr;
-    p.expert_ids = nullptr;
-    p.ntpp = nullptr;
-    p.M = pin.M2;
-    p.a_rows = pin.M2;
-    p.C = pin.C2;
-    p.c_row_offset = pin.c2_row_offset;
-    p.topk_w = nullptr;
+  int mb, nt;
+  const uint16_t* We;
+  int64_t a_bytes, w_bytes;   // bytes the A / W descriptors may reach
+  if (pin.nseg > 0) {
+    // segmented reduction: segment s is a dense product over its own columns
+    const int per = ntn * pin.mblocks;
+    const int tg = xcd_tile(blockIdx.x, per * pin.nseg);
+    const int sg = tg / per, r = tg - sg * per;
+    mb = r % pin.mblocks;
+    nt = r / pin.mblocks;
+    const int beg = pin.seg_beg[sg];
+    p.K = pin.seg_end[sg] - beg;
+    p.A = pin.A + beg;
+    We = pin.W + beg;
+    p.C = (char*)pin.C + sg * pin.seg_c_stride * (pin.c_fp32 ? 4 : 2);
+    a_bytes = ((int64_t)p.a_rows * p.lda - beg) * 2;
+    w_bytes = ((int64_t)p.N * p.ldw - beg) * 2;
+  } else {
+    const int tg = xcd_tile(blockIdx.x, ntn * (pin.mblocks + pin.nsb));
+    // tiles past the routed ones belong to the dense second part
+    const bool second = tg >= ntn * pin.mblocks;
+    if (second) {
+      p.A = pin.A2;
+      p.W = pin.W2;
+      p.E = 1;
+      p.a_row_div = 0;
+      p.sorted_ids = nullptr;
+      p.expert_ids = nullptr;
+      p.ntpp = nullptr;
+      p.M = pin.M2;
+      p.a_rows = pin.M2;
+      p.C = pin.C2;
+      p.c_row_offset = pin.c2_row_offset;
+      p.topk_w = nullptr;
+    }
+    const int nmb = second ? pin.nsb : pin.mblocks;
+    const int t = second ? tg - ntn * pin.mblocks : tg;
+    const int total_rows = p.ntpp ? *p.ntpp : p.M;
+    const int vb = min(nmb, (total_rows + BM - 1) / BM);   // m-blocks holding rows
+    const int mb0 = t / ntn;
+    if (mb0 >= vb) return;
+    int rs = 0, re = vb;
+    if (p.expert_ids) expert_run(p.expert_ids, mb0, vb, lane, rs, re);
+    constexpr int GM = MOE_GM;
+    const int jr = t - rs * ntn;
+    const int grp = jr / (GM * ntn);
+    const int gsz = min(GM, re - rs - grp * GM);
+    const int j = jr - grp * GM * ntn;
+    mb = rs + grp * GM + j % gsz;
+    nt = j / gsz;
+    const int e = p.expert_ids ? p.expert_ids[mb] : 0;
+    if (e < 0 || e >= p.E) return;
+    We = p.W + (int64_t)e * p.N * p.ldw;
+    a_bytes = (int64_t)p.a_rows * p.lda * 2;
+    w_bytes = (int64_t)p.N * p.ldw * 2;
   }
-  const int nmb = second ? pin.nsb : pin.mblocks;
-  const int t = second ? tg - ntn * pin.mblocks : tg;
-  const int total_rows = p.ntpp ? *p.ntpp : p.M;
-  const int vb = min(nmb, (total_rows + BM - 1) / BM);   // m-blocks holding rows
-  const int mb0 = t / ntn;
-  if (mb0 >= vb) return;
-  int rs = 0, re = vb;
-  if (p.expert_ids) expert_run(p.expert_ids, mb0, vb, lane, rs, re);
-  constexpr int GM = MOE_GM;
-  const int jr = t - rs * ntn;
-  const int grp = jr / (GM * ntn);
-  const int gsz = min(GM, re - rs - grp * GM);
-  const int j = jr - grp * GM * ntn;
-  const int mb = rs + grp * GM + j % gsz;
-  const int nt = j / gsz;
-
   const int m0 = mb * BM;
-  const int e = p.expert_ids ? p.expert_ids[mb] : 0;
-  if (e < 0 || e >= p.E) return;
-  const uint16_t* We = p.W + (int64_t)e * p.N * p.K;
   const int ncols = SW ? p.I : p.N;           // output columns
   const int n0 = nt * (SW ? BNW / 2 : BNW);
 
@@ -233,7 +253,7 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) grouped_gemm_ker
         } else if (i < p.M) {
           arow = i;
         }
-        if (arow >= 0) xdo[q] = arow * p.K * 2 + c * 16;
+        if (arow >= 0) xdo[q] = arow * p.lda * 2 + c * 16;
       }
     }
 #pragma unroll
@@ -251,7 +271,7 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) grouped_gemm_ker
         g = n0 + r;
         ok = g < p.N;
       }
-      wdo[q] = ok ? g * p.K * 2 + c * 16 : kNoRow;
+      wdo[q] = ok ? g * p.ldw * 2 + c * 16 : kNoRow;
     }
   }
 
@@ -292,8 +312,8 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) grouped_gemm_ker
     const uint64_t a = (uint64_t)base;
     return i32x4{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xffffu), (int)bytes, 0x00020000};
   };
-  const i32x4 xr4 = rsrc4(p.A, (int64_t)p.a_rows * p.K * 2);
-  const i32x4 wr4 = rsrc4(We, (int64_t)p.N * p.K * 2);
+  const i32x4 xr4 = rsrc4(p.A, a_bytes);
+  const i32x4 wr4 = rsrc4(We, w_bytes);
   auto dma1 = [](const i32x4& rs, const void* lds, int voff, int soff) {
     const unsigned la = (unsigned)(uintptr_t)(const __attribute__((address_space(3))) void*)lds;
     int m0save;
@@ -492,7 +512,8 @@ hipError_t launch_bm(GemmParams p, hipStream_t s) {
   p.mblocks = (p.M + BM - 1) / BM;
   p.nsb = p.M2 > 0 ? (p.M2 + BM - 1) / BM : 0;
   p.ntiles_n = (ncols + tile_n - 1) / tile_n;
-  const int64_t nwg = (int64_t)(p.mblocks + p.nsb) * p.ntiles_n;
+  if (p.nseg > 0) p.nsb = 0;
+  const int64_t nwg = (int64_t)(p.mblocks + p.nsb) * p.ntiles_n * (p.nseg > 0 ? p.nseg : 1);
   if (nwg == 0) return hipSuccess;
   if (sw)
     hipLaunchKernelGGL((grouped_gemm_kernel<BM, BNW, WAVES_M, WAVES_N, true, BK, NS, MINW>),

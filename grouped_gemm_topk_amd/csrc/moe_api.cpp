@@ -238,7 +238,116 @@ int moe_grouped_gemm(const moe_gemm_args* args, void* workspace, size_t* workspa
   p.c_row_offset = 0;
   p.ldc = g.epilogue == MOE_EPI_SWIGLU ? g.N / 2 : g.N;
   p.a_rows = g.a_row_div > 0 ? g.num_valid / g.a_row_div : g.capacity;
+  p.lda = p.ldw = g.K;
   return hip_status(moe::launch_grouped_gemm(p, g.block_m, (hipStream_t)stream));
+}
+
+int moe_grouped_gemm_backward(const moe_gemm_backward_args* args, void* workspace,
+                              size_t* workspace_bytes, void* stream) {
+  if (!args || !workspace_bytes) return MOE_ERR_NULL;
+  const moe_gemm_backward_args& g = *args;
+  if (g.M < 0 || g.E < 1 || g.E > MOE_MAX_EXPERTS || g.N <= 0 || g.K <= 0) return MOE_ERR_SHAPE;
+  if (g.K % 8 != 0 || g.N % 8 != 0) return MOE_ERR_SHAPE;
+  if (!valid_bm(g.block_m)) return MOE_ERR_SHAPE;
+  if (g.out_fp32 != 0 && g.out_fp32 != 1) return MOE_ERR_SHAPE;
+  if (g.capacity < 0 || g.capacity % g.block_m != 0 ||
+      g.capacity < MOE_ALIGN_CAPACITY((int64_t)g.M, 1, g.E, g.block_m))
+    return MOE_ERR_CAPACITY;
+  const int64_t cap = g.capacity;
+  {  // 32-bit byte offsets inside every operand the kernels address
+    if ((int64_t)g.M * g.K * 2 >= kMaxBufferBytes || (int64_t)g.M * g.N * 2 >= kMaxBufferBytes ||
+        (int64_t)g.N * g.K * 2 >= kMaxBufferBytes || (int64_t)g.N * cap * 2 >= kMaxBufferBytes ||
+        (int64_t)g.K * cap * 2 >= kMaxBufferBytes || cap / 64 >= 65535)
+      return MOE_ERR_UNSUPPORTED;
+  }
+  // workspace: wt [E, K, N] (dx); dyt [N, cap], xt [K, cap], seg table (dw)
+  Carver c(workspace);
+  uint16_t* wt = g.dx ? (uint16_t*)c.take((size_t)g.E * g.N * g.K * 2) : nullptr;
+  uint16_t* dyt = g.dw ? (uint16_t*)c.take((size_t)g.N * cap * 2) : nullptr;
+  uint16_t* xt = g.dw ? (uint16_t*)c.take((size_t)g.K * cap * 2) : nullptr;
+  int* seg = g.dw ? (int*)c.take((size_t)2 * g.E * sizeof(int)) : nullptr;
+  if (!workspace) {
+    *workspace_bytes = c.off;
+    return MOE_OK;
+  }
+  if (*workspace_bytes < c.off) return MOE_ERR_CAPACITY;
+  if (!g.dx && !g.dw) return MOE_OK;
+  // with no rows there is nothing to read but the layout's (empty) block table
+  if (!g.expert_ids || !g.num_tokens_post_padded) return MOE_ERR_NULL;
+  if (g.M > 0 && (!g.sorted_token_ids || !g.dy)) return MOE_ERR_NULL;
+  if (g.M > 0 && g.dx && !g.w) return MOE_ERR_NULL;
+  if (g.M > 0 && g.dw && !g.x) return MOE_ERR_NULL;
+  if ((g.dx && (!aligned16(g.dx) || !aligned16(g.w))) || (g.dw && (!aligned16(g.dw) || !aligned16(g.x))) ||
+      !aligned16(g.dy) || !aligned16(workspace))
+    return MOE_ERR_ALIGN;
+  int st = check_device();
+  if (st != MOE_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipSuccess;
+  if (g.dx && g.M > 0) {
+    // dx = dy . w[e]: the aligned grouped GEMM of dy's rows against w^T
+    // ([E, K, N], reduction along N), scattered back to row order
+    e = moe::launch_transpose((const uint16_t*)g.w, wt, g.E, g.N, g.K, s);
+    if (e != hipSuccess) return hip_status(e);
+    moe::GemmParams p{};
+    p.A = (const uint16_t*)g.dy;
+    p.a_row_div = 1;
+    p.W = wt;
+    p.E = g.E;
+    p.N = g.K;
+    p.K = g.N;
+    p.I = g.K;
+    p.sorted_ids = g.sorted_token_ids;
+    p.expert_ids = g.expert_ids;
+    p.ntpp = g.num_tokens_post_padded;
+    p.M = g.capacity;
+    p.num_valid = g.M;
+    p.epi = MOE_EPI_WEIGHTED_SCATTER;
+    p.topk_w = nullptr;
+    p.C = g.dx;
+    p.c_fp32 = g.out_fp32;
+    p.ldc = g.K;
+    p.a_rows = g.M;
+    p.lda = p.ldw = g.N;
+    e = moe::launch_grouped_gemm(p, g.block_m, s);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  if (g.dw) {
+    // dw[e] = dyt[:, window e] . xt[:, window e]^T over the expert's padded
+    // positions (pads are zero columns), one segment per expert
+    e = moe::launch_seg_table(g.expert_ids, g.num_tokens_post_padded, g.block_m, g.E, seg,
+                              seg + g.E, s);
+    if (e == hipSuccess)
+      e = moe::launch_gather_transpose((const uint16_t*)g.dy, g.N, g.sorted_token_ids,
+                                       g.num_tokens_post_padded, g.M, 1, (int)cap, dyt, (int)cap, s);
+    if (e == hipSuccess)
+      e = moe::launch_gather_transpose((const uint16_t*)g.x, g.K, g.sorted_token_ids,
+                                       g.num_tokens_post_padded, g.M, 1, (int)cap, xt, (int)cap, s);
+    if (e != hipSuccess) return hip_status(e);
+    moe::GemmParams p{};
+    p.A = dyt;
+    p.a_row_div = 0;
+    p.W = xt;
+    p.E = 1;
+    p.N = g.K;
+    p.K = 0;
+    p.I = g.K;
+    p.M = g.N;
+    p.num_valid = g.N;
+    p.epi = MOE_EPI_STORE;
+    p.C = g.dw;
+    p.c_fp32 = g.out_fp32;
+    p.ldc = g.K;
+    p.a_rows = g.N;
+    p.lda = p.ldw = (int)cap;
+    p.nseg = g.E;
+    p.seg_beg = seg;
+    p.seg_end = seg + g.E;
+    p.seg_c_stride = (int64_t)g.N * g.K;
+    e = moe::launch_grouped_gemm(p, 128, s);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  return MOE_OK;
 }
 
 int moe_fused_forward(const moe_layer_params* p, const void* x, const float* router_logits,
@@ -357,6 +466,7 @@ int moe_fused_forward(const moe_layer_params* p, const void* x, const float* rou
   g1.c_fp32 = 0;
   g1.ldc = I;
   g1.a_rows = T;
+  g1.lda = g1.ldw = H;
   if (p->n_shared) {   // the shared expert's tiles ride in the same launch
     g1.A2 = (const uint16_t*)x;
     g1.W2 = (const uint16_t*)shared_w13;
@@ -387,6 +497,7 @@ int moe_fused_forward(const moe_layer_params* p, const void* x, const float* rou
   g2.c_row_offset = 0;
   g2.ldc = H;
   g2.a_rows = (int)cap;
+  g2.lda = g2.ldw = I;
   if (p->n_shared) {   // shared-expert rows T*k + t, weight 1, same launch
     g2.A2 = L.act_sh;
     g2.W2 = (const uint16_t*)shared_w2;

@@ -70,6 +70,15 @@ struct GemmParams {
   void* C2;
   int64_t c2_row_offset;
   int mblocks, nsb, ntiles_n;   // tile grid: routed and second-part m-blocks (set by the launcher)
+  // row strides (elements) of A and W; the forward uses K for both
+  int lda, ldw;
+  // segmented reduction (nseg > 0): nseg independent dense products, segment s
+  // reducing over columns [seg_beg[s], seg_end[s]) of A and W (K is ignored)
+  // into C + s * seg_c_stride elements; no gather, no second part
+  int nseg;
+  const int* seg_beg;
+  const int* seg_end;
+  int64_t seg_c_stride;
 };
 
 // ---------------------------------------------------------------- decode GEMVs
@@ -104,6 +113,17 @@ hipError_t launch_gate(const GateParams& p, hipStream_t s);
 hipError_t launch_route_fused(const GateParams& g, const AlignParams& a, hipStream_t s);
 hipError_t launch_align(const AlignParams& p, hipStream_t s);
 hipError_t launch_grouped_gemm(const GemmParams& p, int block_m, hipStream_t s);
+// bf16 [B, R, C] -> [B, C, R] (R and C multiples of 8)
+hipError_t launch_transpose(const uint16_t* src, uint16_t* dst, int B, int R, int C, hipStream_t s);
+// dst [C, ld] column j = row of src for padded position j < *ntpp: row
+// sorted[j] / div (sorted[j] < num_valid) or zeros (a pad); C multiple of 8
+hipError_t launch_gather_transpose(const uint16_t* src, int C, const int* sorted, const int* ntpp,
+                                   int num_valid, int div, int cap, uint16_t* dst, int ld,
+                                   hipStream_t s);
+// seg_beg / seg_end of every expert's run of blocks in the aligned layout
+// (padded positions; both 0 for an expert without blocks)
+hipError_t launch_seg_table(const int* expert_ids, const int* ntpp, int block_m, int E,
+                            int* seg_beg, int* seg_end, hipStream_t s);
 hipError_t launch_combine(const float* yslot, int T, int k, int H, int has_shared, float* out,
                           hipStream_t s);
 

@@ -23,8 +23,8 @@ SCORE_SOFTMAX, SCORE_SIGMOID = 0, 1
 ACT_SWIGLU, ACT_RELU2 = 0, 1
 EPI_STORE, EPI_SWIGLU, EPI_RELU2, EPI_WEIGHTED_SCATTER = 0, 1, 2, 3
 
-EXPORTED = ("moe_align", "moe_grouped_gemm", "moe_fused_forward", "moe_align_capacity",
-            "moe_status_string")
+EXPORTED = ("moe_align", "moe_grouped_gemm", "moe_grouped_gemm_backward", "moe_fused_forward",
+            "moe_align_capacity", "moe_status_string")
 
 
 class MoeError(RuntimeError):
@@ -52,6 +52,15 @@ class MoeGemmArgs(ctypes.Structure):
                 ("c", ctypes.c_void_p), ("c_is_fp32", ctypes.c_int32)]
 
 
+class MoeGemmBackwardArgs(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("w", ctypes.c_void_p), ("dy", ctypes.c_void_p),
+                ("M", ctypes.c_int32), ("E", ctypes.c_int32), ("N", ctypes.c_int32),
+                ("K", ctypes.c_int32), ("sorted_token_ids", ctypes.c_void_p),
+                ("expert_ids", ctypes.c_void_p), ("num_tokens_post_padded", ctypes.c_void_p),
+                ("block_m", ctypes.c_int32), ("capacity", ctypes.c_int32), ("dx", ctypes.c_void_p),
+                ("dw", ctypes.c_void_p), ("out_fp32", ctypes.c_int32)]
+
+
 _lib = None
 
 
@@ -67,6 +76,8 @@ def lib() -> ctypes.CDLL:
         L.moe_align.restype = ctypes.c_int
         L.moe_grouped_gemm.argtypes = [ctypes.POINTER(MoeGemmArgs), vp, sz, vp]
         L.moe_grouped_gemm.restype = ctypes.c_int
+        L.moe_grouped_gemm_backward.argtypes = [ctypes.POINTER(MoeGemmBackwardArgs), vp, sz, vp]
+        L.moe_grouped_gemm_backward.restype = ctypes.c_int
         L.moe_fused_forward.argtypes = [ctypes.POINTER(MoeLayerParams), vp, vp, vp, vp, vp, vp,
                                         vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moe_fused_forward.restype = ctypes.c_int
@@ -221,6 +232,46 @@ class IndexedGroupedGemm:
     def run(self, stream=None) -> torch.Tensor:
         self.align(stream)
         return self.gemm(stream)
+
+    def backward(self, dy: torch.Tensor, dx: Optional[torch.Tensor] = None,
+                 dw: Optional[torch.Tensor] = None, want_dx: bool = True, want_dw: bool = True,
+                 out_fp32: bool = False, stream=None):
+        """Gradients for the output gradient ``dy`` (bf16 [M, N]) through
+        ``moe_grouped_gemm_backward``: returns ``(dx, dw)`` (bf16, or float32
+        with ``out_fp32``; None where not wanted).  Uses the aligned layout of
+        the last ``align()``/``run()``; the workspace is kept between calls."""
+        G, N, K = self.w.shape
+        _dev(dy, "dy", torch.bfloat16, (self.M, N))
+        dt = torch.float32 if out_fp32 else torch.bfloat16
+        dev = dy.device
+        if want_dx and dx is None:
+            dx = torch.empty((self.M, K), dtype=dt, device=dev)
+        if want_dw and dw is None:
+            dw = torch.empty((G, N, K), dtype=dt, device=dev)
+        if dx is not None:
+            _dev(dx, "dx", dt, (self.M, K))
+        if dw is not None:
+            _dev(dw, "dw", dt, (G, N, K))
+        args = MoeGemmBackwardArgs(x=_ptr(self.x), w=_ptr(self.w), dy=_ptr(dy), M=self.M, E=G, N=N,
+                                   K=K, sorted_token_ids=_ptr(self.sorted),
+                                   expert_ids=_ptr(self.expert_ids),
+                                   num_tokens_post_padded=_ptr(self.ntpp), block_m=self.block_m,
+                                   capacity=self.sorted.numel(), dx=_ptr(dx) if want_dx else None,
+                                   dw=_ptr(dw) if want_dw else None, out_fp32=int(out_fp32))
+        n = ctypes.c_size_t(0)
+        L = lib()
+        _check("moe_grouped_gemm_backward",
+               L.moe_grouped_gemm_backward(ctypes.byref(args), None, ctypes.byref(n), None))
+        key = (want_dx, want_dw)
+        ws = getattr(self, "_bwd_ws", {}).get(key)
+        if ws is None or ws.numel() < n.value:
+            ws = _workspace(n.value, dev)
+            self._bwd_ws = {**getattr(self, "_bwd_ws", {}), key: ws}
+        n = ctypes.c_size_t(ws.numel())
+        _check("moe_grouped_gemm_backward",
+               L.moe_grouped_gemm_backward(ctypes.byref(args), _ptr(ws), ctypes.byref(n),
+                                           _stream(stream)))
+        return (dx if want_dx else None), (dw if want_dw else None)
 
 
 def indexed_grouped_gemm(x: torch.Tensor, w: torch.Tensor, expert_indices: torch.Tensor,

@@ -213,7 +213,7 @@ def small_config(name: str = "small", **kw) -> MoEConfig:
 # ---------------------------------------------------------------------------
 # standalone grouped GEMM (rows mapped to experts by an index per row)
 # ---------------------------------------------------------------------------
-_TID_GX, _TID_GW, _TID_GPERM = 11, 12, 13
+_TID_GX, _TID_GW, _TID_GPERM, _TID_GDY = 11, 12, 13, 14
 
 
 @dataclasses.dataclass(frozen=True)
@@ -257,9 +257,11 @@ def small_gemm_scenario(name: str = "cg_small", **kw) -> GemmScenario:
     return GemmScenario(**base)
 
 
-def make_gemm_inputs(sc: GemmScenario, threads: Optional[int] = None) -> Dict[str, np.ndarray]:
+def make_gemm_inputs(sc: GemmScenario, threads: Optional[int] = None,
+                     with_grad: bool = False) -> Dict[str, np.ndarray]:
     """``x`` (bf16 bits [M, K]), ``w`` (bf16 bits [G, N, K], one stream per
-    expert) and ``expert_indices`` (int32 [M])."""
+    expert) and ``expert_indices`` (int32 [M]); with ``with_grad`` also an
+    output gradient ``dy`` (bf16 bits [M, N], N(0, 1))."""
     if sc.sizes is not None:
         sizes = np.asarray(sc.sizes, dtype=np.int64)
         if sizes.size != sc.G or int(sizes.sum()) != sc.M:
@@ -279,5 +281,8 @@ def make_gemm_inputs(sc: GemmScenario, threads: Optional[int] = None) -> Dict[st
     nthreads = threads or min(16, len(os.sched_getaffinity(0)))
     with ThreadPoolExecutor(max(1, nthreads)) as ex:
         list(ex.map(fill, range(sc.G)))
-    return {"x": _normal_bf16((sc.M, sc.K), 1.0, sc.family, sc.M, _TID_GX),
-            "w": w, "expert_indices": np.ascontiguousarray(idx)}
+    out = {"x": _normal_bf16((sc.M, sc.K), 1.0, sc.family, sc.M, _TID_GX),
+           "w": w, "expert_indices": np.ascontiguousarray(idx)}
+    if with_grad:
+        out["dy"] = _normal_bf16((sc.M, sc.N), 1.0, sc.family, sc.M, _TID_GDY)
+    return out

@@ -141,6 +141,52 @@ int moe_grouped_gemm(const moe_gemm_args* args, void* workspace, size_t* workspa
                      void* stream);
 
 /*
+ * Gradients of the indexed grouped GEMM out[i] = x[i] . w[idx[i]]^T (the
+ * axolotl page's cg_backward.py: cg_grouped_gemm_backward_inputs and
+ * cg_grouped_gemm_backward_weights), for an output gradient dy:
+ *
+ *   dx[i] = dy[i] . w[idx[i]]                                   [M, K]
+ *   dw[e] = sum over rows i with idx[i] == e of dy[i]^T x[i]     [E, N, K]
+ *           (zero for an expert without rows)
+ *
+ * fp32 accumulation; output bf16 (round to nearest even) or fp32.  The rows'
+ * grouping is the aligned layout moe_align produces for the per-row expert
+ * indices with top_k = 1 (T = M); any grouping works (empty experts,
+ * non-contiguous indices).
+ *
+ * Arguments (device pointers, row-major, 16-byte aligned; bf16 = raw uint16):
+ *   x   [M, K], w [E, N, K], dy [M, N]; K and N multiples of 8
+ *   sorted_token_ids, expert_ids, num_tokens_post_padded, block_m, capacity:
+ *       moe_align's outputs for the indices (capacity = the sorted ids'
+ *       length, at least MOE_ALIGN_CAPACITY(M, 1, E, block_m))
+ *   dx  [M, K] or NULL (not computed); dw [E, N, K] or NULL (not computed)
+ *   out_fp32: 1 fp32 outputs, 0 bf16
+ * Workspace (CUB convention; NULL = size query): the transposed weights for
+ * dx (E * N * K bf16), and for dw the gathered, transposed dy and x in the
+ * aligned order (N * capacity and K * capacity bf16) plus a per-expert table.
+ * Errors: as moe_grouped_gemm; a transposed operand above 2 GiB returns
+ * MOE_ERR_UNSUPPORTED.  M = 0 writes dw = 0 (when requested) and nothing else;
+ * x, dy, w and sorted_token_ids may then be NULL.
+ */
+typedef struct {
+  const void* x;
+  const void* w;
+  const void* dy;
+  int32_t M, E, N, K;
+  const int32_t* sorted_token_ids;
+  const int32_t* expert_ids;
+  const int32_t* num_tokens_post_padded;
+  int32_t block_m;
+  int32_t capacity;
+  void* dx;
+  void* dw;
+  int32_t out_fp32;
+} moe_gemm_backward_args;
+
+int moe_grouped_gemm_backward(const moe_gemm_backward_args* args, void* workspace,
+                              size_t* workspace_bytes, void* stream);
+
+/*
  * The whole routed MoE layer: gating -> align -> GEMM1 + activation ->
  * GEMM2 + routed weight -> combine (the axolotl DeepSeek-V3 MoE forward
  * `_moe_triton_forward`, fused; the skill card's recipe end to end).

@@ -349,7 +349,7 @@ def indexed_grouped_gemm(x: np.ndarray, w: np.ndarray, expert_indices: np.ndarra
 
 
 def indexed_grouped_gemm_backward(x: np.ndarray, w: np.ndarray, expert_indices: np.ndarray,
-                                  dy: np.ndarray):
+                                  dy: np.ndarray, dx_rows=None, dw_rows=None):
     """Gradients of the indexed grouped GEMM ``out[i] = x[i] @ w[idx[i]].T``
     for an output gradient ``dy`` (the axolotl page's ``cg_backward.py``:
     ``cg_grouped_gemm_backward_inputs`` and ``..._weights``):
@@ -358,11 +358,24 @@ def indexed_grouped_gemm_backward(x: np.ndarray, w: np.ndarray, expert_indices: 
         dw[e] = sum over rows i with idx[i] == e of outer(dy[i], x[i])
               = dy[rows_e].T @ x[rows_e]                ([E, N, K]; zero if no rows)
 
-    Read per row, like the forward.  One matmul per expert, float64."""
+    Read per row, like the forward.  One matmul per expert, float64.
+
+    Spot checks of large cases: ``dx_rows`` (row ids) and ``dw_rows`` ((e, n)
+    pairs) return only those rows of dx and dw, each from the same
+    definition: ``(dx[dx_rows], [dw[e, n] for e, n in dw_rows])``."""
+    idx = np.asarray(expert_indices).reshape(-1)
+    if dx_rows is not None or dw_rows is not None:
+        sx = [np.asarray(dy[r], np.float64) @ np.asarray(w[int(idx[r])], np.float64)
+              for r in (dx_rows if dx_rows is not None else [])]
+        sw = []
+        for e, n in (dw_rows if dw_rows is not None else []):
+            sel = np.nonzero(idx == e)[0]
+            sw.append(np.asarray(dy[sel, n], np.float64) @ np.asarray(x[sel], np.float64)
+                      if sel.size else np.zeros(np.shape(x)[1]))
+        return np.array(sx), np.array(sw)
     x = np.asarray(x, dtype=np.float64)
     w = np.asarray(w, dtype=np.float64)
     dy = np.asarray(dy, dtype=np.float64)
-    idx = np.asarray(expert_indices).reshape(-1)
     E, N, K = w.shape
     dx = np.full((x.shape[0], K), np.nan)
     dw = np.zeros((E, N, K))

@@ -161,3 +161,38 @@ def test_grouped_gemm_validation(L):
     assert call(epilogue=3, capacity=0) == 0   # scatter without weights is valid (weight 1)
     assert call(w=fake + 8) == -5
     assert call(capacity=0) == 0           # nothing to do
+
+
+def test_grouped_gemm_backward_validation_and_sizes(L):
+    fake = 1 << 20
+    M_, E, N, K, bm = 100, 4, 64, 96, 32
+    cap = L.moe_align_capacity(M_, 1, E, bm)
+    base = dict(x=fake, w=fake, dy=fake, M=M_, E=E, N=N, K=K, sorted_token_ids=fake,
+                expert_ids=fake, num_tokens_post_padded=fake, block_m=bm, capacity=cap,
+                dx=fake, dw=fake, out_fp32=0)
+
+    def call(ws=None, n=0, **kw):
+        d = dict(base)
+        d.update(kw)
+        args = M.MoeGemmBackwardArgs(**d)
+        sz = ctypes.c_size_t(n)
+        st = L.moe_grouped_gemm_backward(ctypes.byref(args), ws, ctypes.byref(sz), None)
+        return st, sz.value
+
+    r = lambda b: (b + 255) // 256 * 256
+    assert call(dw=None) == (0, r(E * N * K * 2))
+    assert call(dx=None) == (0, r(N * cap * 2) + r(K * cap * 2) + r(2 * E * 4))
+    assert call() == (0, r(E * N * K * 2) + r(N * cap * 2) + r(K * cap * 2) + r(2 * E * 4))
+    assert call(K=60)[0] == -2
+    assert call(N=12)[0] == -2
+    assert call(E=0)[0] == -2
+    assert call(block_m=48)[0] == -2
+    assert call(capacity=cap - bm)[0] == -3          # below MOE_ALIGN_CAPACITY
+    assert call(ws=fake, n=10)[0] == -3              # workspace too small
+    assert call(ws=fake, n=1 << 30, dx=None, dw=None)[0] == 0   # nothing requested: no launch
+    assert call(ws=fake, n=1 << 30, dy=None)[0] == -1
+    assert call(ws=fake, n=1 << 30, dw=None, w=None)[0] == -1
+    assert call(ws=fake, n=1 << 30, dx=None, x=None)[0] == -1
+    assert call(ws=fake, n=1 << 30, expert_ids=None)[0] == -1
+    assert call(ws=fake + 8, n=1 << 30)[0] == -5
+    assert L.moe_grouped_gemm_backward(None, None, None, None) == -1

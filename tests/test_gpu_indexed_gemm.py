@@ -134,3 +134,75 @@ def test_indexed_grouped_gemm_graph_replays(moe):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, eager), f"replay {rep}"
+
+
+# ---------------------------------------------------------------- backward
+BWD_SMALL = SMALL + [
+    W.small_gemm_scenario("cg_bwd_g6_uneven", G=6, M=900, N=264, K=136,
+                          sizes=(0, 400, 1, 250, 0, 249), block_m=64),
+    W.small_gemm_scenario("cg_bwd_empty_rows", G=3, M=0, N=64, K=64, sizes=(0, 0, 0)),
+]
+
+
+@pytest.mark.parametrize("sc", BWD_SMALL, ids=[s.name for s in BWD_SMALL])
+@pytest.mark.parametrize("fp32", [False, True], ids=["bf16", "fp32"])
+def test_indexed_grouped_gemm_backward_small(moe, sc, fp32):
+    print(f"indexed grouped gemm backward {sc.name} fp32={fp32}", flush=True)
+    inp = W.make_gemm_inputs(sc, with_grad=True)
+    x64, w64, dy64 = (O.bf16_to_f64(inp[k]) for k in ("x", "w", "dy"))
+    rdx, rdw = O.indexed_grouped_gemm_backward(x64, w64, inp["expert_indices"], dy64)
+    op = moe.IndexedGroupedGemm(to_dev(inp["x"]), to_dev(inp["w"]), to_dev(inp["expert_indices"]),
+                                sc.block_m)
+    op.align()
+    dt = torch.float32 if fp32 else torch.bfloat16
+    dx = torch.full((sc.M, sc.K), float("nan"), dtype=dt, device="cuda")
+    dw = torch.full((sc.G, sc.N, sc.K), float("nan"), dtype=dt, device="cuda")
+    op.backward(to_dev(inp["dy"]), dx, dw, out_fp32=fp32)
+    torch.cuda.synchronize()
+    gx, gw = dx.float().cpu().numpy(), dw.float().cpu().numpy()
+    assert np.all(np.isfinite(gx)) and np.all(np.isfinite(gw)), "outputs left unwritten"
+    if sc.M:
+        assert not (np.abs(gx - rdx) > _tol(rdx, fp32)).any(), f"dx worst {np.abs(gx - rdx).max()}"
+    tw = _tol(rdw, fp32) if np.abs(rdw).max() > 0 else 0.0
+    assert not (np.abs(gw - rdw) > tw).any(), f"dw worst {np.abs(gw - rdw).max()}"
+
+
+def test_indexed_grouped_gemm_backward_one_side(moe):
+    """dx alone and dw alone (the other pointer NULL) give the same values."""
+    sc = W.small_gemm_scenario("cg_bwd_sides", sizes=(100, 200, 180))
+    inp = W.make_gemm_inputs(sc, with_grad=True)
+    op = moe.IndexedGroupedGemm(to_dev(inp["x"]), to_dev(inp["w"]), to_dev(inp["expert_indices"]),
+                                sc.block_m)
+    op.align()
+    dy = to_dev(inp["dy"])
+    dx_both, dw_both = op.backward(dy)
+    dx_only, none_w = op.backward(dy, want_dw=False)
+    none_x, dw_only = op.backward(dy, want_dx=False)
+    torch.cuda.synchronize()
+    assert none_w is None and none_x is None
+    assert torch.equal(dx_both, dx_only) and torch.equal(dw_both, dw_only)
+
+
+@pytest.mark.parametrize("sc", FULL, ids=[s.name for s in FULL])
+def test_indexed_grouped_gemm_backward_full_size_sampled(moe, sc):
+    print(f"indexed grouped gemm backward full size {sc.name}", flush=True)
+    inp = W.make_gemm_inputs(sc, with_grad=True)
+    op = moe.IndexedGroupedGemm(to_dev(inp["x"]), to_dev(inp["w"]), to_dev(inp["expert_indices"]),
+                                sc.block_m)
+    op.align()
+    dx = torch.full((sc.M, sc.K), float("nan"), dtype=torch.bfloat16, device="cuda")
+    dw = torch.full((sc.G, sc.N, sc.K), float("nan"), dtype=torch.bfloat16, device="cuda")
+    op.backward(to_dev(inp["dy"]), dx, dw)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(dx).all()) and bool(torch.isfinite(dw).all()), "outputs left unwritten"
+    idx = inp["expert_indices"]
+    rng = np.random.default_rng(12)
+    starts = np.flatnonzero(np.r_[True, idx[1:] != idx[:-1]])
+    xrows = np.unique(np.r_[starts, np.r_[starts[1:], sc.M] - 1, rng.integers(0, sc.M, 16)])
+    wrows = [(e, int(n)) for e in range(sc.G) for n in np.r_[0, sc.N - 1, rng.integers(0, sc.N, 2)]]
+    sx, sw = O.indexed_grouped_gemm_backward(O.bf16_to_f64(inp["x"]), O.bf16_to_f64(inp["w"]), idx,
+                                             O.bf16_to_f64(inp["dy"]), dx_rows=xrows, dw_rows=wrows)
+    gx = dx[torch.from_numpy(xrows).cuda()].float().cpu().numpy()
+    gw = np.stack([dw[e, n].float().cpu().numpy() for e, n in wrows])
+    assert not (np.abs(gx - sx) > _tol(sx, False)).any(), f"dx worst {np.abs(gx - sx).max()}"
+    assert not (np.abs(gw - sw) > _tol(sw, False)).any(), f"dw worst {np.abs(gw - sw).max()}"

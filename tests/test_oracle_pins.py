@@ -498,3 +498,14 @@ def test_indexed_backward_matches_autograd():
     dx, dw = O.indexed_grouped_gemm_backward(x, w, idx, dy)
     np.testing.assert_allclose(dx, xt.grad.numpy(), rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(dw, wt.grad.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_indexed_backward_sampled_rows_match_full():
+    rng = np.random.default_rng(18)
+    M, K, N, E = 25, 8, 6, 3
+    x, w, dy = rng.standard_normal((M, K)), rng.standard_normal((E, N, K)), rng.standard_normal((M, N))
+    idx = np.r_[np.zeros(10, int), np.full(15, 2)]       # expert 1 empty
+    dx, dw = O.indexed_grouped_gemm_backward(x, w, idx, dy)
+    sx, sw = O.indexed_grouped_gemm_backward(x, w, idx, dy, dx_rows=[3, 24], dw_rows=[(0, 5), (1, 0), (2, 2)])
+    np.testing.assert_allclose(sx, dx[[3, 24]], rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(sw, np.stack([dw[0, 5], dw[1, 0], dw[2, 2]]), rtol=1e-13, atol=1e-13)
