@@ -24,6 +24,16 @@
 //   workgroup and reduced in LDS.
 // * GEMV2 adds weight * result into `out` with fp32 atomics (the k slots of a
 //   token arrive in any order); GEMV1 zeroes `out` first.
+// * From kFusedMinSlots slots on, a second path: a one-workgroup route kernel
+//   (routing, zeroing `out`, resetting per-block counters), then one launch in
+//   which the first workgroups do the W13 GEMV and count themselves done per
+//   block, and the rest request their W2 weights at once, wait for their
+//   block's count and finish.  The activation rows cross between them with
+//   device-coherent 8-byte stores and loads, which need no cache maintenance
+//   (an acquire per poll invalidated the L2 and was seven times slower; one
+//   shared counter serialised every workgroup's atomic).  The W2 stream then
+//   overlaps the W13 one, which pays once the W13 phase is long (larger T);
+//   for a handful of slots the separate, prologue-carrying GEMV1 is faster.
 #include <hip/hip_runtime.h>
 #include <limits.h>
 
@@ -353,6 +363,26 @@ __device__ __forceinline__ void token_operands(const uint16_t* row, int k0, int 
   }
 }
 
+// token_operands for rows another workgroup of the same launch wrote: 8-byte
+// device-coherent loads, which never return a stale L2 copy (the writer used
+// device-coherent stores and counted itself done after they completed)
+__device__ __forceinline__ void token_operands_coherent(const uint16_t* row, int k0, int K,
+                                                        u32x4 (&xb)[8]) {
+  const int kg = k0 + 8 * ((threadIdx.x & 63) >> 4);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int kc = kg + 32 * q;
+    if (row && kc < K) {
+      const uint64_t* p8 = (const uint64_t*)(row + kc);
+      const uint64_t lo = __hip_atomic_load(p8, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint64_t hi = __hip_atomic_load(p8 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      xb[q] = u32x4{(unsigned)lo, (unsigned)(lo >> 32), (unsigned)hi, (unsigned)(hi >> 32)};
+    } else {
+      xb[q] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+}
+
 __device__ __forceinline__ f32x4 tile_mfma(const u32x4* lds, const u32x4 (&xb)[8], f32x4 acc) {
 #pragma unroll
   for (int q = 0; q < 8; ++q) acc = mfma16(tile_operand(lds, q), xb[q], acc);
@@ -386,6 +416,45 @@ __device__ __forceinline__ f32x4 stream_rounds(__amdgpu_buffer_rsrc_t rs, int K,
     acc = tile_mfma(tl, xb, acc);
     wave_sync_lds();
     rd = nrd2;
+  }
+  return acc;
+}
+
+// K rounds kp, kp + S, ... of one tile against one token row.  The caller
+// has issued the loads of the first two rounds (stream_begin) into cur / nxt;
+// each round's weight tile is consumed while the round two steps later is in
+// flight, so every wave keeps two tiles of loads outstanding.
+__device__ __forceinline__ void stream_begin(__amdgpu_buffer_rsrc_t rs, int K, int kp, int S,
+                                             int rounds, u32x4 (&cur)[8], u32x4 (&nxt)[8]) {
+  if (kp < rounds) tile_load(rs, K, kp * kRound, K, cur);
+  if (kp + S < rounds) tile_load(rs, K, (kp + S) * kRound, K, nxt);
+}
+
+template <bool COHERENT>
+__device__ __forceinline__ f32x4 stream_finish(__amdgpu_buffer_rsrc_t rs, int K,
+                                               const uint16_t* brow, int kp, int S, int rounds,
+                                               u32x4* tl, f32x4 acc, u32x4 (&cur)[8],
+                                               u32x4 (&nxt)[8]) {
+  u32x4 xb[8];
+  int rd = kp;
+  while (rd < rounds) {
+    if (COHERENT) token_operands_coherent(brow, rd * kRound, K, xb);
+    else token_operands(brow, rd * kRound, K, xb);
+    tile_store(tl, cur);
+    wave_sync_lds();
+    acc = tile_mfma(tl, xb, acc);
+    wave_sync_lds();
+    if (rd + 2 * S < rounds) tile_load(rs, K, (rd + 2 * S) * kRound, K, cur);
+    rd += S;
+    if (rd >= rounds) break;
+    if (COHERENT) token_operands_coherent(brow, rd * kRound, K, xb);
+    else token_operands(brow, rd * kRound, K, xb);
+    tile_store(tl, nxt);
+    wave_sync_lds();
+    acc = tile_mfma(tl, xb, acc);
+    wave_sync_lds();
+    if (rd + 2 * S < rounds) tile_load(rs, K, (rd + 2 * S) * kRound, K, nxt);
+    rd += S;
   }
   return acc;
 }
@@ -535,6 +604,194 @@ __global__ void __launch_bounds__(kG2Waves * 64) gemv2_kernel(GemvParams p) {
     if (h0 + 4 * g + v < p.H) unsafeAtomicAdd(dst + v, wgt * acc[v]);
 }
 
+// ------------------------------------------------------------------ fused path (larger T)
+constexpr int kWaves = kPrologueWaves;   // waves of every decode workgroup
+// slots (T * top_k) from which the fused path runs: measured on MI355X, the
+// separate W2 launch is cheaper at 8 and 24 slots (128 experts top-8, T = 1, 3
+// and top-6, T = 1), the fused launch at 64 and 96 (T = 8 top-8, T = 16 top-6)
+constexpr int kFusedMinSlots = 48;
+
+// Control block in the layer workspace, reset by route_kernel before every
+// decode_kernel launch: per block b (routed blocks, then the shared expert),
+// the number of W13 workgroups of b that are done, each counter on its own
+// 128-byte line so that the blocks' atomics do not queue behind each other.
+constexpr int kCtlStride = 32;
+// bound of the W2 workgroups' wait (polls about half a microsecond apart,
+// about a second in all): far above any W13 phase, so a stuck counter ends
+// the wait instead of the process (the output is then wrong, never hung)
+constexpr int kMaxSpin = 1 << 21;
+constexpr int kSpinSleep = 16;   // s_sleep units of 64 cycles between polls
+
+// Routing for all T <= 16 tokens by one workgroup (gating + align, the
+// outputs the decode kernel and the caller read), then zero `out` (the W2
+// phase accumulates into it) and reset the control block.
+__global__ void __launch_bounds__(kWaves * 64) route_kernel(GemvParams p) {
+  __shared__ RouteLds L;
+  route_prologue(p, L, -1, true);
+  const int64_t n4 = (int64_t)p.T * p.H / 4;
+  for (int64_t i = threadIdx.x; i < n4; i += blockDim.x)
+    ((float4*)p.out)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  const int nb = p.nblk + (p.sw13 ? 1 : 0);
+  for (int b = threadIdx.x; b < nb; b += blockDim.x) p.ctl[b * kCtlStride] = 0;
+}
+
+// The slot of row r of block b, or -1 (a pad or no block); the shared expert's
+// rows are the tokens.
+__device__ __forceinline__ int block_row_slot(const GemvParams& p, int b, bool shared, int r, int ntpp) {
+  if (shared) return r < p.T ? r : -1;
+  if (b * p.bm >= ntpp) return -1;
+  const int sid = p.sorted_ids[b * p.bm + r];
+  return (sid >= 0 && sid < p.T * p.k) ? sid : -1;
+}
+
+// W13 phase, one workgroup: p.nt1 tiles of 16 act columns at once, each tile
+// on kWaves / p.nt1 waves (SwiGLU: half on the gate rows, half on the up
+// rows) that split K.  act[row j of block b][c0 + 0..15] = act(x[token of row
+// j] . w13[e] rows).
+template <bool SW>
+__device__ void w13_phase(const GemvParams& p, int bx, int b, u32x4 (*s_tile)[kTileU4], int* s_slot) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const bool shared = b == p.nblk;
+  const int ntpp = *p.ntpp;
+  if (tid < 16) s_slot[tid] = block_row_slot(p, b, shared, tid, ntpp);
+  const int e = shared ? 0 : (b * p.bm < ntpp ? p.expert_ids[b] : -1);
+  __syncthreads();
+  if (!shared && (e < 0 || e >= p.E)) return;
+  const int r = lane & 15;   // token column of this lane (operand and result)
+  const int g = lane >> 4;
+  const int slot = s_slot[r];
+  const int M1 = SW ? 2 * p.I : p.I;
+  const uint16_t* W = shared ? p.sw13 : p.w13 + (int64_t)e * M1 * p.H;
+  const int tok = slot < 0 ? -1 : (shared ? slot : slot / p.k);
+  const uint16_t* xrow = tok >= 0 ? p.x + (int64_t)tok * p.H : nullptr;
+  u32x4* tl = s_tile[wave];
+  const int rounds = (p.H + kRound - 1) / kRound;
+  const int per = kWaves / p.nt1;
+  const int S = SW ? per / 2 : per;
+  const int ti = wave / per;
+  const int wi = wave % per;
+  const bool up = SW && wi >= S;
+  const int kp = wi % S;
+  const int c0 = (bx * p.nt1 + ti) * 16;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (c0 < p.I) {
+    const __amdgpu_buffer_rsrc_t rs =
+        tile_rsrc(W + (int64_t)((up ? p.I : 0) + c0) * p.H, p.H, p.I - c0);
+    u32x4 cur[8], nxt[8];
+    stream_begin(rs, p.H, kp, S, rounds, cur, nxt);
+    acc = stream_finish<false>(rs, p.H, xrow, kp, S, rounds, tl, acc, cur, nxt);
+  }
+  ((f32x4*)tl)[lane] = acc;   // partial sums reuse the wave's own tile buffer
+  __syncthreads();
+  if (wi != 0 || c0 >= p.I || slot < 0 || c0 + 4 * g >= p.I) return;
+  f32x4 hg = acc, hu = {0.f, 0.f, 0.f, 0.f};
+  for (int w = 1; w < per; ++w) {
+    const f32x4 o = ((const f32x4*)s_tile[wave + w])[lane];
+    if (SW && w >= S) hu += o; else hg += o;
+  }
+  // lane holds act columns c0 + 4 g + v of token column r
+  float o4[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    if (SW) {
+      o4[v] = silu(hg[v]) * hu[v];
+    } else {
+      float t = fmaxf(hg[v], 0.f);
+      o4[v] = t * t;
+    }
+  }
+  uint16_t* dst = shared ? p.act_sh + (int64_t)r * p.I : p.act + (int64_t)(b * p.bm + r) * p.I;
+  const uint64_t lo = (uint64_t)f32_to_bf16(o4[0]) | ((uint64_t)f32_to_bf16(o4[1]) << 16);
+  const uint64_t hi = (uint64_t)f32_to_bf16(o4[2]) | ((uint64_t)f32_to_bf16(o4[3]) << 16);
+  // device-coherent store: the W2 phase of this launch reads it from another CU
+  __hip_atomic_store((uint64_t*)(dst + c0 + 4 * g), lo | (hi << 32), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// W2 phase, one workgroup: p.nt2 tiles of 16 output rows at once, each on
+// kWaves / p.nt2 waves that split K; out[token of row j][h0 + ..] +=
+// w_slot * (act[row j] . w2[e][h]).  The first two rounds of weights are
+// requested before the wait for the W13 phase, so they arrive while it runs.
+__device__ void w2_phase(const GemvParams& p, int bx, int b, int g1x, u32x4 (*s_tile)[kTileU4],
+                         int* s_slot) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const bool shared = b == p.nblk;
+  const int ntpp = *p.ntpp;
+  if (tid < 16) s_slot[tid] = block_row_slot(p, b, shared, tid, ntpp);
+  const int e = shared ? 0 : (b * p.bm < ntpp ? p.expert_ids[b] : -1);
+  const bool active = shared || (e >= 0 && e < p.E);
+  const uint16_t* W = shared ? p.sw2 : p.w2 + (int64_t)(active ? e : 0) * p.H * p.I;
+  const int rounds = (p.I + kRound - 1) / kRound;
+  const int S = kWaves / p.nt2;
+  const int ti = wave / S;
+  const int kp = wave % S;
+  const int h0 = (bx * p.nt2 + ti) * 16;
+  const bool work = active && h0 < p.H;
+  const __amdgpu_buffer_rsrc_t rs = tile_rsrc(W + (int64_t)(work ? h0 : 0) * p.I, p.I,
+                                              work ? p.H - h0 : 0);
+  u32x4 cur[8], nxt[8];
+  if (work) stream_begin(rs, p.I, kp, S, rounds, cur, nxt);
+  // wait until the g1x W13 workgroups of this block have published its act rows
+  if (tid == 0 && active) {
+    int spins = 0;
+    while (__hip_atomic_load(&p.ctl[b * kCtlStride], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
+               g1x &&
+           ++spins < kMaxSpin)
+      __builtin_amdgcn_s_sleep(kSpinSleep);
+  }
+  __syncthreads();   // the act rows are then read with device-coherent loads
+  if (!active) return;
+  const int r = lane & 15;
+  const int g = lane >> 4;
+  const int slot = s_slot[r];
+  const uint16_t* arow = nullptr;
+  if (slot >= 0) arow = shared ? p.act_sh + (int64_t)r * p.I : p.act + (int64_t)(b * p.bm + r) * p.I;
+  u32x4* tl = s_tile[wave];
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (work) acc = stream_finish<true>(rs, p.I, arow, kp, S, rounds, tl, acc, cur, nxt);
+  ((f32x4*)tl)[lane] = acc;
+  __syncthreads();
+  if (kp != 0 || !work || slot < 0) return;
+  for (int w = wave + 1; w < wave + S; ++w) acc += ((const f32x4*)s_tile[w])[lane];
+  const int tok = shared ? slot : slot / p.k;
+  const float wgt = shared ? 1.f : p.topk_w[slot];
+  // lane holds rows h0 + 4 g + v of token column r
+  float* dst = p.out + (int64_t)tok * p.H + h0 + 4 * g;
+#pragma unroll
+  for (int v = 0; v < 4; ++v)
+    if (h0 + 4 * g + v < p.H) unsafeAtomicAdd(dst + v, wgt * acc[v]);
+}
+
+// Both GEMVs in one launch.  Workgroups [0, n1 = g1x * nb) do the W13 phase
+// (tile bx, block b) and count themselves done in their block's counter; the
+// rest do the W2 phase of a block, which waits for that block's count.
+// Workgroups are dispatched in index order, so every W13 workgroup is running
+// or finished before a W2 workgroup waits (and the wait is bounded).
+template <bool SW>
+__global__ void __launch_bounds__(kWaves * 64) decode_kernel(GemvParams p, int g1x, int g2x) {
+  __shared__ u32x4 s_tile[kWaves][kTileU4];
+  __shared__ int s_slot[16];
+  const int nb = p.nblk + (p.sw13 ? 1 : 0);
+  const int n1 = g1x * nb;
+  const int t = blockIdx.x;
+  if (t < n1) {
+    const int b = t / g1x;
+    w13_phase<SW>(p, t % g1x, b, s_tile, s_slot);
+    // every thread's device-coherent act stores have completed before the count
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (threadIdx.x == 0)
+      __hip_atomic_fetch_add(&p.ctl[b * kCtlStride], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+    const int t2 = t - n1;
+    w2_phase(p, t2 % g2x, t2 / g2x, g1x, s_tile, s_slot);
+  }
+}
+
 }  // namespace
 
 // Tiles per workgroup: the largest power of two (up to the wave count) that
@@ -552,12 +809,25 @@ hipError_t launch_gemv(const GemvParams& p0, bool swiglu, hipStream_t s) {
   const int tiles2 = (p.H + 15) / 16;
   p.nt1 = pick_tiles((int64_t)tiles1 * nb, swiglu ? kG1Waves / 2 : kG1Waves, 768);
   p.nt2 = pick_tiles((int64_t)tiles2 * nb, kG2Waves, 768);
-  dim3 g1((tiles1 + p.nt1 - 1) / p.nt1, nb);
+  const int g1x = (tiles1 + p.nt1 - 1) / p.nt1;
+  const int g2x = (tiles2 + p.nt2 - 1) / p.nt2;
+  if (p.T * p.k >= kFusedMinSlots) {
+    // route once, then both GEMVs in one launch with the W2 weights requested
+    // while the W13 phase runs
+    hipLaunchKernelGGL(route_kernel, dim3(1), dim3(kWaves * 64), 0, s, p);
+    const unsigned nwg = (unsigned)((g1x + g2x) * nb);
+    if (swiglu)
+      hipLaunchKernelGGL(decode_kernel<true>, dim3(nwg), dim3(kWaves * 64), 0, s, p, g1x, g2x);
+    else
+      hipLaunchKernelGGL(decode_kernel<false>, dim3(nwg), dim3(kWaves * 64), 0, s, p, g1x, g2x);
+    return hipGetLastError();
+  }
+  dim3 g1(g1x, nb);
   if (swiglu)
     hipLaunchKernelGGL(gemv1_kernel<true>, g1, dim3(kG1Waves * 64), 0, s, p);
   else
     hipLaunchKernelGGL(gemv1_kernel<false>, g1, dim3(kG1Waves * 64), 0, s, p);
-  dim3 g2((tiles2 + p.nt2 - 1) / p.nt2, nb);
+  dim3 g2(g2x, nb);
   hipLaunchKernelGGL(gemv2_kernel, g2, dim3(kG2Waves * 64), 0, s, p);
   return hipGetLastError();
 }

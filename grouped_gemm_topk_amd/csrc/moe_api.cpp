@@ -104,6 +104,7 @@ struct LayerWorkspace {
   int32_t* align_scratch;
   uint16_t* act;      // [cap, I] bf16 in padded order
   uint16_t* act_sh;   // [T, I] bf16, shared expert
+  int32_t* ctl;       // decode kernel's control block
   float* yslot;       // [T*k (+T), H] fp32 weighted expert outputs
   size_t bytes;
 };
@@ -122,6 +123,7 @@ LayerWorkspace layout_layer(const moe_layer_params* p, void* ws) {
   w.act = (uint16_t*)c.take((size_t)cap * p->I * 2);
   w.act_sh = (uint16_t*)c.take((size_t)(p->n_shared ? p->T : 0) * p->I * 2);
   w.yslot = (float*)c.take((size_t)(n + (p->n_shared ? p->T : 0)) * p->H * 4);
+  w.ctl = (int32_t*)c.take((size_t)(moe::kMaxExperts + 1) * 32 * sizeof(int32_t));
   w.bytes = c.off;
   return w;
 }
@@ -420,6 +422,7 @@ int moe_fused_forward(const moe_layer_params* p, const void* x, const float* rou
     gv.act = L.act;
     gv.act_sh = L.act_sh;
     gv.out = out;
+    gv.ctl = L.ctl;
     return hip_status(moe::launch_gemv(gv, p->activation == MOE_ACT_SWIGLU, s));
   }
 

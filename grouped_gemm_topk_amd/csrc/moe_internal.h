@@ -104,7 +104,8 @@ struct GemvParams {
   int nt1, nt2;             // 16-row tiles per workgroup of GEMV1 / GEMV2 (set by the launcher)
   uint16_t* act;            // [capacity, I] rows in padded order
   uint16_t* act_sh;         // [T, I]
-  float* out;               // [T, H], zeroed by GEMV1, accumulated by GEMV2
+  float* out;               // [T, H], zeroed by GEMV1 or the route kernel, accumulated by the W2 GEMV
+  int* ctl;                 // control block of the decode kernel (workspace, reset every call)
 };
 
 hipError_t launch_gemv(const GemvParams& p, bool swiglu, hipStream_t s);

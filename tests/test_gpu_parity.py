@@ -163,6 +163,13 @@ SMALL = [
     W.small_config("small_relu2_t16", T=16, H=264, I=40, E=32, top_k=6, activation=W.ACT_RELU2),
     W.small_config("small_t17_gemm", T=17, H=64, I=48, E=8, top_k=2),
     W.small_config("small_decode_ragged_k", T=3, H=600, I=328, E=64, top_k=8),
+    # the decode path's two forms: from 48 slots (T * top_k) one fused launch,
+    # below it GEMV1 + GEMV2; the boundary on both sides, and the fused form
+    # with grouped routing and the shared expert (its own block and counter)
+    W.small_config("small_decode_fused_edge", T=6, H=128, I=64, E=64, top_k=8),
+    W.small_config("small_decode_below_fused", T=15, H=128, I=64, E=32, top_k=3),
+    W.small_config("small_dsv3_decode_fused", T=14, H=136, I=72, E=18, top_k=4,
+                   scoring=W.SCORE_SIGMOID, n_group=6, topk_group=4, n_shared=1, block_m=16),
     # the largest expert count and top-k the ABI accepts, on both paths
     W.small_config("small_max_e_k", T=20, H=64, I=32, E=256, top_k=16),
     W.small_config("small_max_e_k_decode", T=4, H=64, I=32, E=256, top_k=16),
