@@ -107,12 +107,14 @@ __device__ __forceinline__ void rank_keys(const uint64_t* row, int n, const uint
   }
 }
 
-constexpr int kPrologueWaves = 4;
+constexpr int kPrologueWaves = 4;     // waves of GEMV1, which carries the prologue
+constexpr int kRouteWaves = 16;       // waves of the route kernel: one per token
 
-struct RouteLds {
-  float wlog[kPrologueWaves][kRow];     // per-wave copy of one token's logits
-  uint64_t key[kPrologueWaves][kRow];   // per-wave order keys of one token
-  double gscore[kPrologueWaves][64];
+template <int NW>
+struct RouteLdsT {
+  float wlog[NW][kRow];     // per-wave copy of one token's logits
+  uint64_t key[NW][kRow];   // per-wave order keys of one token
+  double gscore[NW][64];
   double ex[kMaxSlots];        // per-slot exp / sigmoid terms of the weights
   int ids[kMaxSlots];
   float val[kMaxSlots];
@@ -124,11 +126,14 @@ struct RouteLds {
   int ntpp;
   int my_expert;               // expert of this workgroup's block, -1 if none
 };
+typedef RouteLdsT<kPrologueWaves> RouteLds;
 
-// Gating + align for all T <= 16 tokens by one workgroup of kPrologueWaves
+// Gating + align for all T <= 16 tokens by one workgroup of NW waves (one
+// token per wave at a time)
 // waves.  Fills `L` and, when `write_out`, the routing outputs in global
 // memory.  `blk` is the block whose rows this workgroup needs (or -1).
-__device__ void route_prologue(const GemvParams& p, RouteLds& L, int blk, bool write_out) {
+template <int NW>
+__device__ void route_prologue(const GemvParams& p, RouteLdsT<NW>& L, int blk, bool write_out) {
   const int tid = threadIdx.x;
   const int nthr = blockDim.x;
   const int lane = tid & 63;
@@ -144,7 +149,7 @@ __device__ void route_prologue(const GemvParams& p, RouteLds& L, int blk, bool w
   // ---- gating: one wave per token
   float* wl = L.wlog[wave];
   uint64_t* wk = L.key[wave];
-  for (int t = wave; t < T; t += kPrologueWaves) {
+  for (int t = wave; t < T; t += NW) {
     float v[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -625,8 +630,8 @@ constexpr int kSpinSleep = 16;   // s_sleep units of 64 cycles between polls
 // Routing for all T <= 16 tokens by one workgroup (gating + align, the
 // outputs the decode kernel and the caller read), then zero `out` (the W2
 // phase accumulates into it) and reset the control block.
-__global__ void __launch_bounds__(kWaves * 64) route_kernel(GemvParams p) {
-  __shared__ RouteLds L;
+__global__ void __launch_bounds__(kRouteWaves * 64) route_kernel(GemvParams p) {
+  __shared__ RouteLdsT<kRouteWaves> L;
   route_prologue(p, L, -1, true);
   const int64_t n4 = (int64_t)p.T * p.H / 4;
   for (int64_t i = threadIdx.x; i < n4; i += blockDim.x)
@@ -814,7 +819,7 @@ hipError_t launch_gemv(const GemvParams& p0, bool swiglu, hipStream_t s) {
   if (p.T * p.k >= kFusedMinSlots) {
     // route once, then both GEMVs in one launch with the W2 weights requested
     // while the W13 phase runs
-    hipLaunchKernelGGL(route_kernel, dim3(1), dim3(kWaves * 64), 0, s, p);
+    hipLaunchKernelGGL(route_kernel, dim3(1), dim3(kRouteWaves * 64), 0, s, p);
     const unsigned nwg = (unsigned)((g1x + g2x) * nb);
     if (swiglu)
       hipLaunchKernelGGL(decode_kernel<true>, dim3(nwg), dim3(kWaves * 64), 0, s, p, g1x, g2x);
