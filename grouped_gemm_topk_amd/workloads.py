@@ -286,3 +286,52 @@ def make_gemm_inputs(sc: GemmScenario, threads: Optional[int] = None,
     if with_grad:
         out["dy"] = _normal_bf16((sc.M, sc.N), 1.0, sc.family, sc.M, _TID_GDY)
     return out
+
+
+# ---------------------------------------------------------------------------
+# MXFP8 expert weights (decode): an input format, produced from the bf16 weights
+# ---------------------------------------------------------------------------
+MX_BLOCK = 32          # elements per shared scale (OCP Microscaling)
+E4M3_MAX = 448.0       # largest finite FP8 E4M3 value
+
+
+def quantize_mxfp8(bits: np.ndarray):
+    """bf16 weights [..., K] (K a multiple of 32) -> (FP8 E4M3 bits [..., K]
+    uint8, E8M0 scale bits [..., K / 32] uint8), the way a bf16 checkpoint is
+    converted to MXFP8 (OCP Microscaling): per block of 32 consecutive
+    elements along K, the smallest power-of-two scale 2^x with max |w| / 2^x
+    <= 448 (so no element saturates), elements w / 2^x rounded to
+    nearest-even E4M3; an all-zero block gets scale bits 0.  Quantisation
+    happens before the library (like any checkpoint conversion); the library
+    and the oracle only decode."""
+    import torch
+    shp = bits.shape
+    if shp[-1] % MX_BLOCK:
+        raise ValueError("K must be a multiple of 32")
+    w = bf16_bits_to_f32(bits).reshape(*shp[:-1], shp[-1] // MX_BLOCK, MX_BLOCK)
+    amax = np.abs(w).max(axis=-1)
+    with np.errstate(divide="ignore"):
+        shared = np.where(amax > 0, np.ceil(np.log2(np.where(amax > 0, amax, 1.0) / E4M3_MAX)),
+                          -127.0)
+    sbits = np.clip(shared + 127, 0, 254).astype(np.uint8)
+    scale = np.ldexp(np.float32(1.0), sbits.astype(np.int32) - 127).astype(np.float32)
+    scaled = np.clip(w / scale[..., None], -E4M3_MAX, E4M3_MAX)
+    q = torch.from_numpy(np.ascontiguousarray(scaled, dtype=np.float32)).to(torch.float8_e4m3fn)
+    return q.view(torch.uint8).numpy().reshape(shp), sbits
+
+
+def make_mxfp8_weights(inp: Dict[str, np.ndarray]) -> Dict[str, np.ndarray]:
+    """MXFP8 forms of the layer's weights, expert by expert: w13_q / w13_s,
+    w2_q / w2_s and, with a shared expert, shared_w13_q / _s, shared_w2_q / _s."""
+    out: Dict[str, np.ndarray] = {}
+    for name in ("w13", "w2"):
+        w = inp[name]
+        q = np.empty(w.shape, dtype=np.uint8)
+        s = np.empty(w.shape[:-1] + (w.shape[-1] // MX_BLOCK,), dtype=np.uint8)
+        for e in range(w.shape[0]):
+            q[e], s[e] = quantize_mxfp8(w[e])
+        out[name + "_q"], out[name + "_s"] = q, s
+    for name in ("shared_w13", "shared_w2"):
+        if name in inp:
+            out[name + "_q"], out[name + "_s"] = quantize_mxfp8(inp[name])
+    return out

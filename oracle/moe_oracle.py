@@ -387,6 +387,32 @@ def indexed_grouped_gemm_backward(x: np.ndarray, w: np.ndarray, expert_indices: 
     return dx, dw
 
 
+def e4m3_to_f64(bits: np.ndarray) -> np.ndarray:
+    """FP8 E4M3 ("fn": no infinities) bits -> float64, from the format's
+    definition (OCP 8-bit floating point): sign, 4 exponent bits with bias 7,
+    3 mantissa bits; exponent 0 is subnormal (m/8 * 2^-6); S.1111.111 is NaN."""
+    b = np.asarray(bits, dtype=np.uint8).astype(np.int64)
+    s = np.where(b >> 7, -1.0, 1.0)
+    e = (b >> 3) & 0xF
+    m = (b & 7).astype(np.float64)
+    val = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    val = np.where((e == 15) & (m == 7), np.nan, val)
+    return s * val
+
+
+def e8m0_to_f64(bits: np.ndarray) -> np.ndarray:
+    """E8M0 scale bits -> 2^(bits - 127) (255 is NaN), OCP Microscaling."""
+    b = np.asarray(bits, dtype=np.uint8).astype(np.float64)
+    return np.where(b == 255, np.nan, np.exp2(b - 127.0))
+
+
+def mxfp8_to_f64(q: np.ndarray, s: np.ndarray, block: int = 32) -> np.ndarray:
+    """MXFP8 weights [..., K] (E4M3 bits) with E8M0 scales [..., K / block]:
+    every element times the scale of its block of ``block`` elements along K."""
+    v = e4m3_to_f64(q)
+    return v * np.repeat(e8m0_to_f64(s), block, axis=-1)
+
+
 # ----------------------------------------------------------------------------
 # the whole layer
 # ----------------------------------------------------------------------------
@@ -419,6 +445,34 @@ def moe_forward_cfg(cfg, inp: Dict[str, np.ndarray]) -> Dict[str, np.ndarray]:
                        n_group=cfg.n_group, topk_group=cfg.topk_group,
                        renormalize=cfg.renormalize, scale=cfg.scale,
                        activation_kind=cfg.activation, n_shared=cfg.n_shared)
+
+
+class _MxExperts:
+    """Expert weights kept in MXFP8 and decoded (mxfp8_to_f64) one expert at a
+    time when the loop asks for it."""
+
+    def __init__(self, q: np.ndarray, s: np.ndarray):
+        self.q, self.s, self.shape = q, s, q.shape
+
+    def __getitem__(self, e):
+        return mxfp8_to_f64(self.q[e], self.s[e])
+
+
+def moe_forward_mxfp8_cfg(cfg, inp: Dict[str, np.ndarray], mx: Dict[str, np.ndarray]):
+    """The layer with MXFP8 expert weights (``mx``: w13_q/_s, w2_q/_s and the
+    shared expert's): the same gating, align and per-expert loop as
+    ``moe_forward``, on the weights the MXFP8 encoding represents."""
+    logits = np.asarray(inp["logits"], dtype=np.float32)
+    ids, wts = gate(logits, cfg.top_k, cfg.scoring, cfg.n_group, cfg.topk_group, cfg.renormalize,
+                    cfg.scale)
+    al = align(ids, logits.shape[1], cfg.block_m)
+    sw13 = sw2 = None
+    if cfg.n_shared:
+        sw13 = mxfp8_to_f64(mx["shared_w13_q"], mx["shared_w13_s"])
+        sw2 = mxfp8_to_f64(mx["shared_w2_q"], mx["shared_w2_s"])
+    out = expert_loop(bf16_to_f64(inp["x"]), _MxExperts(mx["w13_q"], mx["w13_s"]),
+                      _MxExperts(mx["w2_q"], mx["w2_s"]), ids, wts, cfg.activation, sw13, sw2)
+    return {"topk_ids": ids, "topk_weights": wts, **al, "out": out}
 
 
 def token_output(inp: Dict[str, np.ndarray], t: int, ids_t: np.ndarray, wts_t: np.ndarray,

@@ -509,3 +509,62 @@ def test_indexed_backward_sampled_rows_match_full():
     sx, sw = O.indexed_grouped_gemm_backward(x, w, idx, dy, dx_rows=[3, 24], dw_rows=[(0, 5), (1, 0), (2, 2)])
     np.testing.assert_allclose(sx, dx[[3, 24]], rtol=1e-13, atol=1e-13)
     np.testing.assert_allclose(sw, np.stack([dw[0, 5], dw[1, 0], dw[2, 2]]), rtol=1e-13, atol=1e-13)
+
+
+# ---------------------------------------------------------------- MXFP8 decoding
+def test_e4m3_decoding_matches_torch_and_hand_values():
+    bits = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(bits).view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    got = O.e4m3_to_f64(bits)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    fin = ~np.isnan(ref)
+    assert np.array_equal(got[fin], ref[fin])
+    # hand values: 1.0, the largest, the smallest subnormal, -2, NaN
+    assert O.e4m3_to_f64(np.uint8(0x38)) == 1.0
+    assert O.e4m3_to_f64(np.uint8(0x7E)) == 448.0
+    assert O.e4m3_to_f64(np.uint8(0x01)) == 2.0 ** -9
+    assert O.e4m3_to_f64(np.uint8(0xC0)) == -2.0
+    assert np.isnan(O.e4m3_to_f64(np.uint8(0x7F)))
+
+
+def test_e8m0_and_block_scaling():
+    assert O.e8m0_to_f64(np.uint8(127)) == 1.0
+    assert O.e8m0_to_f64(np.uint8(0)) == 2.0 ** -127
+    assert O.e8m0_to_f64(np.uint8(130)) == 8.0
+    assert np.isnan(O.e8m0_to_f64(np.uint8(255)))
+    q = np.full((2, 64), 0x38, np.uint8)         # every element 1.0
+    s = np.array([[127, 130], [120, 0]], np.uint8)
+    w = O.mxfp8_to_f64(q, s)
+    assert np.array_equal(w[0, :32], np.ones(32)) and np.array_equal(w[0, 32:], np.full(32, 8.0))
+    assert np.array_equal(w[1, :32], np.full(32, 2.0 ** -7))
+
+
+def test_mxfp8_quantisation_error_is_bounded():
+    """The workload's MXFP8 weights decode (oracle) to within half an E4M3 step
+    of each element: |w - deq| <= 2^-4 |w| for normal elements, 2^-10 * scale
+    below (subnormal E4M3), and no element saturates."""
+    rng = np.random.default_rng(20)
+    wb = W.f32_to_bf16_bits((0.02 * rng.standard_normal((8, 256))).astype(np.float32))
+    q, s = W.quantize_mxfp8(wb)
+    w = W.bf16_bits_to_f32(wb).astype(np.float64)
+    deq = O.mxfp8_to_f64(q, s)
+    scale = np.repeat(O.e8m0_to_f64(s), 32, axis=-1)
+    assert np.all(np.abs(w - deq) <= np.maximum(2.0 ** -4 * np.abs(w), 2.0 ** -10 * scale) + 1e-30)
+    assert np.all(np.abs(deq) <= 448.0 * scale)
+
+
+def test_mxfp8_layer_equals_layer_on_decoded_weights():
+    """The MXFP8 layer is the bf16-input layer run on the decoded weights
+    (exactly representable in bf16: 3 mantissa bits times a power of two)."""
+    cfg = W.small_config("mx_small", T=5, H=64, I=96, E=8, top_k=2, n_shared=1)
+    inp = W.make_inputs(cfg)
+    mx = W.make_mxfp8_weights(inp)
+    got = O.moe_forward_mxfp8_cfg(cfg, inp, mx)["out"]
+    dec = dict(inp)
+    for name in ("w13", "w2", "shared_w13", "shared_w2"):
+        wf = O.mxfp8_to_f64(mx[name + "_q"], mx[name + "_s"]).astype(np.float32)
+        bits = W.f32_to_bf16_bits(wf)
+        assert np.array_equal(W.bf16_bits_to_f32(bits), wf), "decoded MXFP8 is exact in bf16"
+        dec[name] = bits
+    want = O.moe_forward_cfg(cfg, dec)["out"]
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
