@@ -148,24 +148,36 @@ def time_dominant_gemm(cfg, layer, steps, warmup, torch, moe):
     return e0.elapsed_time(e1) / steps
 
 
-def decode_case(name, torch, moe, W, O, reps=20, flush_reps=20):
+def decode_case(name, torch, moe, W, O, reps=20, flush_reps=20, mxfp8=False):
     """µs per layer at decode shape, cycling L distinct copies of the weights
     from a captured graph; cross-checked by timing one layer eagerly with a
     1 GiB copy (4 x the Infinity Cache) between calls, events around the layer
-    alone, so that every call starts with cold caches."""
+    alone, so that every call starts with cold caches.  ``mxfp8``: the layer
+    with MXFP8 expert weights (the touched experts converted)."""
     cfg = W.CONFIGS[name]
     inp = W.make_inputs(cfg)
     ids, _ = O.gate(inp["logits"], cfg.top_k, cfg.scoring, cfg.n_group, cfg.topk_group,
                     cfg.renormalize, cfg.scale)
     touched = int(np.unique(ids).size)
-    per_expert = cfg.mats * cfg.H * cfg.I * 2
+    # bytes per weight: bf16 2; MXFP8 1 plus one scale byte per 32
+    per_expert = cfg.mats * cfg.H * cfg.I * (1 + 1 / 32 if mxfp8 else 2)
     wbytes = touched * per_expert
     nlayers = max(2, int(np.ceil(4 * MALL_BYTES / wbytes)))
-    base = {k: _to_dev(inp[k], torch) for k in ("w13", "w2")}
+    mx = W.make_mxfp8_weights(inp, experts=np.unique(ids).tolist()) if mxfp8 else None
+    if mxfp8:
+        base = {k + s: torch.from_numpy(mx[k + s]).cuda() for k in ("w13", "w2") for s in ("_q", "_s")}
+    else:
+        base = {k: _to_dev(inp[k], torch) for k in ("w13", "w2")}
     layers = []
     for li in range(nlayers):
         w = base if li == 0 else {k: v.clone() for k, v in base.items()}
-        layers.append(_layer(cfg, inp, torch, moe, weights=w)[0])
+        if mxfp8:
+            p = moe.LayerParams.from_config(cfg)
+            layers.append(moe.FusedLayer(p, _to_dev(inp["x"], torch), _to_dev(inp["logits"], torch),
+                                         w["w13_q"], w["w2_q"],
+                                         scales={"w13": w["w13_s"], "w2": w["w2_s"]}))
+        else:
+            layers.append(_layer(cfg, inp, torch, moe, weights=w)[0])
     for l in layers:
         l.run()
     torch.cuda.synchronize()
@@ -206,11 +218,12 @@ def decode_case(name, torch, moe, W, O, reps=20, flush_reps=20):
     # parity of the last layer's output against the oracle (all tokens)
     out = layers[0].run().cpu().numpy()
     torch.cuda.synchronize()
-    ref = O.moe_forward_cfg(cfg, inp)["out"]
+    ref = (O.moe_forward_mxfp8_cfg(cfg, inp, mx) if mxfp8 else O.moe_forward_cfg(cfg, inp))["out"]
     err = float(np.abs(out - ref).max())
     del layers, base
     torch.cuda.empty_cache()
-    return {"config": name, "T": cfg.T, "us_per_layer": round(us, 2),
+    return {"config": name, "weights": "mxfp8" if mxfp8 else "bf16", "T": cfg.T,
+            "us_per_layer": round(us, 2),
             "us_flushed_median": round(us_flushed, 2), "touched_experts": touched,
             "alg_bytes": int(alg_bytes), "GBps": round(gbs, 1),
             "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "layers_cycled": nlayers,
@@ -497,8 +510,9 @@ def main():
                                                                    moe, W)}), flush=True)
         return
     if args.decode_only:
-        print(json.dumps({"decode": [decode_case(n, torch, moe, W, O) for n in DECODE_CASES]}),
-              flush=True)
+        print(json.dumps({"decode": [decode_case(n, torch, moe, W, O) for n in DECODE_CASES],
+                          "decode_mxfp8": [decode_case(n, torch, moe, W, O, mxfp8=True)
+                                           for n in DECODE_CASES]}), flush=True)
         return
     cfg = W.CONFIGS[args.config]
     inp = W.make_inputs(cfg)
@@ -548,8 +562,9 @@ def main():
         line["achievable_peaks"] = peaks
     if not args.no_decode:
         line["decode"] = [decode_case(n, torch, moe, W, O) for n in DECODE_CASES]
+        line["decode_mxfp8"] = [decode_case(n, torch, moe, W, O, mxfp8=True) for n in DECODE_CASES]
         if peaks and "hbm_read_GBps" in peaks:
-            for d in line["decode"]:
+            for d in line["decode"] + line["decode_mxfp8"]:
                 d["frac_of_achievable_hbm"] = round(d["GBps"] / peaks["hbm_read_GBps"], 4)
     if not args.no_gemm_scenarios:
         line["grouped_gemm_scenarios"] = gemm_scenarios(args.steps, args.warmup, torch, moe, W)

@@ -320,35 +320,96 @@ __device__ void route_prologue(const GemvParams& p, RouteLdsT<NW>& L, int blk, b
 // MFMA q covers K elements k0 + 32 q + 8 g + 0..7 for lane group g.
 constexpr int kTileU4 = 16 * 32;   // 16-byte chunks of one tile
 
-// Buffer descriptor over the tile's valid rows (at most 16): loads past them
-// return zero.  DWORD3 0x00020000 = raw 32-bit data format for gfx9 buffers.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* first_row, int64_t ld,
-                                                          int rows_valid) {
-  const int rows = rows_valid < 16 ? rows_valid : 16;
-  return __builtin_amdgcn_make_buffer_rsrc((void*)first_row, (short)0, (int)(rows * ld * 2),
+// One tile's weight rows: bf16, or MXFP8 (Q: FP8 E4M3 bytes, one E8M0 scale
+// byte per 32 elements of a row, OCP Microscaling), which is decoded exactly
+// to bf16 on its way into LDS.  The buffer descriptor covers the tile's valid
+// rows (at most 16), so loads past them return zero.  DWORD3 0x00020000 =
+// raw 32-bit data format for gfx9 buffers.
+struct WSrc {
+  __amdgpu_buffer_rsrc_t rs;
+  int ld;                  // row stride in elements
+  const uint8_t* sc;       // MXFP8: scale row of the tile's first row
+  int rows;                // valid rows (<= 16)
+};
+
+template <bool Q>
+__device__ __forceinline__ WSrc make_wsrc(const void* mat, const uint8_t* scales, int64_t row0,
+                                          int ld, int rows_valid) {
+  WSrc w;
+  w.rows = rows_valid < 16 ? rows_valid : 16;
+  w.ld = ld;
+  constexpr int eb = Q ? 1 : 2;   // bytes per element
+  const char* first = (const char*)mat + row0 * ld * eb;
+  w.rs = __builtin_amdgcn_make_buffer_rsrc((void*)first, (short)0, (int)(w.rows * ld * eb),
                                            0x00020000);
+  w.sc = Q ? scales + row0 * (ld / 32) : nullptr;
+  return w;
 }
 
-__device__ __forceinline__ void tile_load(__amdgpu_buffer_rsrc_t rs, int64_t ld, int k0, int K,
-                                          u32x4 (&v)[8]) {
+// bf16: eight 1 KB wave loads (load j covers tile rows 2j and 2j+1, 32 lanes x
+// 16 bytes).  MXFP8: four 1 KB wave loads (load j covers rows 4j .. 4j+3, 16
+// lanes x 16 elements each) plus each lane's four scale bytes in v[4].
+template <bool Q>
+__device__ __forceinline__ void tile_load(const WSrc& w, int k0, int K, u32x4 (&v)[8]) {
   const int lane = threadIdx.x & 63;
-  const int kc = k0 + 8 * (lane & 31);
-  const int base = (lane >> 5) * (int)ld * 2 + kc * 2;   // byte offset of row (lane >> 5)
-  const int step = 4 * (int)ld;                          // two rows
+  if (!Q) {
+    const int kc = k0 + 8 * (lane & 31);
+    const int base = (lane >> 5) * w.ld * 2 + kc * 2;   // byte offset of row (lane >> 5)
+    const int step = 4 * w.ld;                          // two rows
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int off = kc < K ? base + j * step : -1;     // -1: beyond the descriptor -> zero
-    v[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 2 /* nontemporal */);
+    for (int j = 0; j < 8; ++j) {
+      const int off = kc < K ? base + j * step : -1;     // -1: beyond the descriptor -> zero
+      v[j] = __builtin_amdgcn_raw_buffer_load_b128(w.rs, off, 0, 2 /* nontemporal */);
+    }
+  } else {
+    const int kc = k0 + 16 * (lane & 15);
+    const int r0 = lane >> 4;
+    unsigned sc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = 4 * j + r0;
+      const int off = kc < K ? row * w.ld + kc : -1;
+      v[j] = __builtin_amdgcn_raw_buffer_load_b128(w.rs, off, 0, 2 /* nontemporal */);
+      sc[j] = (kc < K && row < w.rows) ? w.sc[row * (w.ld / 32) + kc / 32] : 0u;
+    }
+    v[4] = u32x4{sc[0], sc[1], sc[2], sc[3]};
   }
 }
 
+// two E4M3 bytes of `four` (the low or the high pair) times the E8M0 scale
+// `s` -> two bf16 (exact: three mantissa bits times a power of two)
+template <bool HI>
+__device__ __forceinline__ unsigned e4m3x2_to_bf16x2(unsigned four, float s) {
+  return __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(four, s, HI));
+}
+
+// The tile in the wave's own LDS buffer, 16-byte chunks of 8 bf16 with the
+// chunk index XOR-ed by the row (row r, chunk c at r * 32 + (c ^ r)).
+template <bool Q>
 __device__ __forceinline__ void tile_store(u32x4* lds, const u32x4 (&v)[8]) {
   const int lane = threadIdx.x & 63;
-  const int ch = lane & 31;
+  if (!Q) {
+    const int ch = lane & 31;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int row = 2 * j + (lane >> 5);
-    lds[row * 32 + (ch ^ row)] = v[j];
+    for (int j = 0; j < 8; ++j) {
+      const int row = 2 * j + (lane >> 5);
+      lds[row * 32 + (ch ^ row)] = v[j];
+    }
+  } else {
+    const int c8 = lane & 15;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = 4 * j + (lane >> 4);
+      // the E8M0 byte is the exponent field of the float scale operand
+      const float s = __builtin_bit_cast(float, v[4][j] << 23);
+      const u32x4 x = v[j];
+      const u32x4 lo = {e4m3x2_to_bf16x2<false>(x.x, s), e4m3x2_to_bf16x2<true>(x.x, s),
+                        e4m3x2_to_bf16x2<false>(x.y, s), e4m3x2_to_bf16x2<true>(x.y, s)};
+      const u32x4 hi = {e4m3x2_to_bf16x2<false>(x.z, s), e4m3x2_to_bf16x2<true>(x.z, s),
+                        e4m3x2_to_bf16x2<false>(x.w, s), e4m3x2_to_bf16x2<true>(x.w, s)};
+      lds[row * 32 + ((2 * c8) ^ row)] = lo;
+      lds[row * 32 + ((2 * c8 + 1) ^ row)] = hi;
+    }
   }
 }
 
@@ -397,26 +458,26 @@ __device__ __forceinline__ f32x4 tile_mfma(const u32x4* lds, const u32x4 (&xb)[8
 // K rounds kp, kp + S, ... of one tile against one token row, with the
 // next round's weight tile requested before the current one is consumed, so
 // that every wave keeps a tile of loads in flight.
-__device__ __forceinline__ f32x4 stream_rounds(__amdgpu_buffer_rsrc_t rs, int K,
-                                               const uint16_t* brow, int kp, int S, int rounds,
-                                               u32x4* tl, f32x4 acc) {
+template <bool Q>
+__device__ __forceinline__ f32x4 stream_rounds(const WSrc& ws, int K, const uint16_t* brow, int kp,
+                                               int S, int rounds, u32x4* tl, f32x4 acc) {
   u32x4 cur[8], nxt[8], xb[8];
   int rd = kp;
-  if (rd < rounds) tile_load(rs, K, rd * kRound, K, cur);
+  if (rd < rounds) tile_load<Q>(ws, rd * kRound, K, cur);
   while (rd < rounds) {
     const int nrd = rd + S;
-    if (nrd < rounds) tile_load(rs, K, nrd * kRound, K, nxt);
+    if (nrd < rounds) tile_load<Q>(ws, nrd * kRound, K, nxt);
     token_operands(brow, rd * kRound, K, xb);
-    tile_store(tl, cur);
+    tile_store<Q>(tl, cur);
     wave_sync_lds();
     acc = tile_mfma(tl, xb, acc);
     wave_sync_lds();
     rd = nrd;
     if (rd >= rounds) break;
     const int nrd2 = rd + S;
-    if (nrd2 < rounds) tile_load(rs, K, nrd2 * kRound, K, cur);
+    if (nrd2 < rounds) tile_load<Q>(ws, nrd2 * kRound, K, cur);
     token_operands(brow, rd * kRound, K, xb);
-    tile_store(tl, nxt);
+    tile_store<Q>(tl, nxt);
     wave_sync_lds();
     acc = tile_mfma(tl, xb, acc);
     wave_sync_lds();
@@ -429,39 +490,63 @@ __device__ __forceinline__ f32x4 stream_rounds(__amdgpu_buffer_rsrc_t rs, int K,
 // has issued the loads of the first two rounds (stream_begin) into cur / nxt;
 // each round's weight tile is consumed while the round two steps later is in
 // flight, so every wave keeps two tiles of loads outstanding.
-__device__ __forceinline__ void stream_begin(__amdgpu_buffer_rsrc_t rs, int K, int kp, int S,
-                                             int rounds, u32x4 (&cur)[8], u32x4 (&nxt)[8]) {
-  if (kp < rounds) tile_load(rs, K, kp * kRound, K, cur);
-  if (kp + S < rounds) tile_load(rs, K, (kp + S) * kRound, K, nxt);
+template <bool Q>
+__device__ __forceinline__ void stream_begin(const WSrc& ws, int K, int kp, int S, int rounds,
+                                             u32x4 (&cur)[8], u32x4 (&nxt)[8]) {
+  if (kp < rounds) tile_load<Q>(ws, kp * kRound, K, cur);
+  if (kp + S < rounds) tile_load<Q>(ws, (kp + S) * kRound, K, nxt);
 }
 
-template <bool COHERENT>
-__device__ __forceinline__ f32x4 stream_finish(__amdgpu_buffer_rsrc_t rs, int K,
-                                               const uint16_t* brow, int kp, int S, int rounds,
-                                               u32x4* tl, f32x4 acc, u32x4 (&cur)[8],
-                                               u32x4 (&nxt)[8]) {
+template <bool Q, bool COHERENT>
+__device__ __forceinline__ f32x4 stream_finish(const WSrc& ws, int K, const uint16_t* brow, int kp,
+                                               int S, int rounds, u32x4* tl, f32x4 acc,
+                                               u32x4 (&cur)[8], u32x4 (&nxt)[8]) {
   u32x4 xb[8];
   int rd = kp;
   while (rd < rounds) {
     if (COHERENT) token_operands_coherent(brow, rd * kRound, K, xb);
     else token_operands(brow, rd * kRound, K, xb);
-    tile_store(tl, cur);
+    tile_store<Q>(tl, cur);
     wave_sync_lds();
     acc = tile_mfma(tl, xb, acc);
     wave_sync_lds();
-    if (rd + 2 * S < rounds) tile_load(rs, K, (rd + 2 * S) * kRound, K, cur);
+    if (rd + 2 * S < rounds) tile_load<Q>(ws, (rd + 2 * S) * kRound, K, cur);
     rd += S;
     if (rd >= rounds) break;
     if (COHERENT) token_operands_coherent(brow, rd * kRound, K, xb);
     else token_operands(brow, rd * kRound, K, xb);
-    tile_store(tl, nxt);
+    tile_store<Q>(tl, nxt);
     wave_sync_lds();
     acc = tile_mfma(tl, xb, acc);
     wave_sync_lds();
-    if (rd + 2 * S < rounds) tile_load(rs, K, (rd + 2 * S) * kRound, K, nxt);
+    if (rd + 2 * S < rounds) tile_load<Q>(ws, (rd + 2 * S) * kRound, K, nxt);
     rd += S;
   }
   return acc;
+}
+
+// The expert matrices of a block: W13 rows [M1, H] or W2 rows [H, I] of expert
+// e (or the shared expert), and with MXFP8 their scale rows.
+template <bool Q>
+__device__ __forceinline__ const void* w13_mat(const GemvParams& p, bool shared, int e, int M1,
+                                               const uint8_t** sc) {
+  if (shared) {
+    *sc = p.sw13_s;
+    return p.sw13;
+  }
+  *sc = Q ? p.w13_s + (int64_t)e * M1 * (p.H / 32) : nullptr;
+  return (const char*)p.w13 + (int64_t)e * M1 * p.H * (Q ? 1 : 2);
+}
+
+template <bool Q>
+__device__ __forceinline__ const void* w2_mat(const GemvParams& p, bool shared, int e,
+                                              const uint8_t** sc) {
+  if (shared) {
+    *sc = p.sw2_s;
+    return p.sw2;
+  }
+  *sc = Q ? p.w2_s + (int64_t)e * p.H * (p.I / 32) : nullptr;
+  return (const char*)p.w2 + (int64_t)e * p.H * p.I * (Q ? 1 : 2);
 }
 
 constexpr int kG1Waves = kPrologueWaves;
@@ -472,7 +557,7 @@ constexpr int kG2Waves = 4;
 // on the up rows) that split K.  act[row j of block b][c0 + 0..15] =
 // act(x[token of row j] . w13[e] rows).  Also zeroes `out`.
 // Grid (ceil(ceil(I/16) / nt1), nblk + shared).
-template <bool SW>
+template <bool SW, bool Q>
 __global__ void __launch_bounds__(kG1Waves * 64) gemv1_kernel(GemvParams p) {
   __shared__ union {
     RouteLds L;
@@ -500,7 +585,8 @@ __global__ void __launch_bounds__(kG1Waves * 64) gemv1_kernel(GemvParams p) {
   __syncthreads();           // the LDS union is reused below
   if (!shared && e < 0) return;
   const int M1 = SW ? 2 * p.I : p.I;
-  const uint16_t* W = shared ? p.sw13 : p.w13 + (int64_t)e * M1 * p.H;
+  const uint8_t* Wsc;
+  const void* W = w13_mat<Q>(p, shared, e, M1, &Wsc);
   const int tok = slot < 0 ? -1 : (shared ? slot : slot / p.k);
   const uint16_t* xrow = tok >= 0 ? p.x + (int64_t)tok * p.H : nullptr;
   u32x4* tl = sm.tile[wave];
@@ -517,9 +603,8 @@ __global__ void __launch_bounds__(kG1Waves * 64) gemv1_kernel(GemvParams p) {
   const int c0 = (blockIdx.x * p.nt1 + ti) * 16;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   if (c0 < p.I) {
-    const __amdgpu_buffer_rsrc_t rs =
-        tile_rsrc(W + (int64_t)((up ? p.I : 0) + c0) * p.H, p.H, p.I - c0);
-    acc = stream_rounds(rs, p.H, xrow, kp, S, rounds, tl, acc);
+    const WSrc ws = make_wsrc<Q>(W, Wsc, (up ? p.I : 0) + c0, p.H, p.I - c0);
+    acc = stream_rounds<Q>(ws, p.H, xrow, kp, S, rounds, tl, acc);
   }
   ((f32x4*)tl)[lane] = acc;   // partial sums reuse the wave's own tile buffer
   __syncthreads();
@@ -550,6 +635,7 @@ __global__ void __launch_bounds__(kG1Waves * 64) gemv1_kernel(GemvParams p) {
 // GEMV2: the workgroup's p.nt2 tiles of 16 output rows at once, each on
 // p.s2 = 4 / p.nt2 waves that split K; out[token of row j][h0 + ..] +=
 // w_slot * (act[row j] . w2[e][h]).  Grid (ceil(ceil(H/16) / nt2), nblk + shared).
+template <bool Q>
 __global__ void __launch_bounds__(kG2Waves * 64) gemv2_kernel(GemvParams p) {
   __shared__ u32x4 s_tile[kG2Waves][kTileU4];
   __shared__ int s_slot[16];
@@ -559,14 +645,15 @@ __global__ void __launch_bounds__(kG2Waves * 64) gemv2_kernel(GemvParams p) {
   const int b = blockIdx.y;
   const bool shared = b == p.nblk;
   const int base = b * p.bm;
-  const uint16_t* W;
+  const uint8_t* Wsc;
+  const void* W;
   if (shared) {
-    W = p.sw2;
+    W = w2_mat<Q>(p, true, 0, &Wsc);
   } else {
     if (base >= *p.ntpp) return;
     const int e = p.expert_ids[b];
     if (e < 0 || e >= p.E) return;
-    W = p.w2 + (int64_t)e * p.H * p.I;
+    W = w2_mat<Q>(p, false, e, &Wsc);
   }
   if (tid < 16) {
     int s = -1;
@@ -593,8 +680,8 @@ __global__ void __launch_bounds__(kG2Waves * 64) gemv2_kernel(GemvParams p) {
   const int h0 = (blockIdx.x * p.nt2 + ti) * 16;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   if (h0 < p.H) {
-    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(W + (int64_t)h0 * p.I, p.I, p.H - h0);
-    acc = stream_rounds(rs, p.I, arow, kp, S, rounds, tl, acc);
+    const WSrc ws = make_wsrc<Q>(W, Wsc, h0, p.I, p.H - h0);
+    acc = stream_rounds<Q>(ws, p.I, arow, kp, S, rounds, tl, acc);
   }
   ((f32x4*)tl)[lane] = acc;
   __syncthreads();
@@ -653,7 +740,7 @@ __device__ __forceinline__ int block_row_slot(const GemvParams& p, int b, bool s
 // on kWaves / p.nt1 waves (SwiGLU: half on the gate rows, half on the up
 // rows) that split K.  act[row j of block b][c0 + 0..15] = act(x[token of row
 // j] . w13[e] rows).
-template <bool SW>
+template <bool SW, bool Q>
 __device__ void w13_phase(const GemvParams& p, int bx, int b, u32x4 (*s_tile)[kTileU4], int* s_slot) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -668,7 +755,8 @@ __device__ void w13_phase(const GemvParams& p, int bx, int b, u32x4 (*s_tile)[kT
   const int g = lane >> 4;
   const int slot = s_slot[r];
   const int M1 = SW ? 2 * p.I : p.I;
-  const uint16_t* W = shared ? p.sw13 : p.w13 + (int64_t)e * M1 * p.H;
+  const uint8_t* Wsc;
+  const void* W = w13_mat<Q>(p, shared, e, M1, &Wsc);
   const int tok = slot < 0 ? -1 : (shared ? slot : slot / p.k);
   const uint16_t* xrow = tok >= 0 ? p.x + (int64_t)tok * p.H : nullptr;
   u32x4* tl = s_tile[wave];
@@ -682,11 +770,10 @@ __device__ void w13_phase(const GemvParams& p, int bx, int b, u32x4 (*s_tile)[kT
   const int c0 = (bx * p.nt1 + ti) * 16;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   if (c0 < p.I) {
-    const __amdgpu_buffer_rsrc_t rs =
-        tile_rsrc(W + (int64_t)((up ? p.I : 0) + c0) * p.H, p.H, p.I - c0);
+    const WSrc ws = make_wsrc<Q>(W, Wsc, (up ? p.I : 0) + c0, p.H, p.I - c0);
     u32x4 cur[8], nxt[8];
-    stream_begin(rs, p.H, kp, S, rounds, cur, nxt);
-    acc = stream_finish<false>(rs, p.H, xrow, kp, S, rounds, tl, acc, cur, nxt);
+    stream_begin<Q>(ws, p.H, kp, S, rounds, cur, nxt);
+    acc = stream_finish<Q, false>(ws, p.H, xrow, kp, S, rounds, tl, acc, cur, nxt);
   }
   ((f32x4*)tl)[lane] = acc;   // partial sums reuse the wave's own tile buffer
   __syncthreads();
@@ -719,6 +806,7 @@ __device__ void w13_phase(const GemvParams& p, int bx, int b, u32x4 (*s_tile)[kT
 // kWaves / p.nt2 waves that split K; out[token of row j][h0 + ..] +=
 // w_slot * (act[row j] . w2[e][h]).  The first two rounds of weights are
 // requested before the wait for the W13 phase, so they arrive while it runs.
+template <bool Q>
 __device__ void w2_phase(const GemvParams& p, int bx, int b, int g1x, u32x4 (*s_tile)[kTileU4],
                          int* s_slot) {
   const int tid = threadIdx.x;
@@ -729,17 +817,17 @@ __device__ void w2_phase(const GemvParams& p, int bx, int b, int g1x, u32x4 (*s_
   if (tid < 16) s_slot[tid] = block_row_slot(p, b, shared, tid, ntpp);
   const int e = shared ? 0 : (b * p.bm < ntpp ? p.expert_ids[b] : -1);
   const bool active = shared || (e >= 0 && e < p.E);
-  const uint16_t* W = shared ? p.sw2 : p.w2 + (int64_t)(active ? e : 0) * p.H * p.I;
+  const uint8_t* Wsc;
+  const void* W = w2_mat<Q>(p, shared, active ? e : 0, &Wsc);
   const int rounds = (p.I + kRound - 1) / kRound;
   const int S = kWaves / p.nt2;
   const int ti = wave / S;
   const int kp = wave % S;
   const int h0 = (bx * p.nt2 + ti) * 16;
   const bool work = active && h0 < p.H;
-  const __amdgpu_buffer_rsrc_t rs = tile_rsrc(W + (int64_t)(work ? h0 : 0) * p.I, p.I,
-                                              work ? p.H - h0 : 0);
+  const WSrc ws = make_wsrc<Q>(W, Wsc, work ? h0 : 0, p.I, work ? p.H - h0 : 0);
   u32x4 cur[8], nxt[8];
-  if (work) stream_begin(rs, p.I, kp, S, rounds, cur, nxt);
+  if (work) stream_begin<Q>(ws, p.I, kp, S, rounds, cur, nxt);
   // wait until the g1x W13 workgroups of this block have published its act rows
   if (tid == 0 && active) {
     int spins = 0;
@@ -757,7 +845,7 @@ __device__ void w2_phase(const GemvParams& p, int bx, int b, int g1x, u32x4 (*s_
   if (slot >= 0) arow = shared ? p.act_sh + (int64_t)r * p.I : p.act + (int64_t)(b * p.bm + r) * p.I;
   u32x4* tl = s_tile[wave];
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  if (work) acc = stream_finish<true>(rs, p.I, arow, kp, S, rounds, tl, acc, cur, nxt);
+  if (work) acc = stream_finish<Q, true>(ws, p.I, arow, kp, S, rounds, tl, acc, cur, nxt);
   ((f32x4*)tl)[lane] = acc;
   __syncthreads();
   if (kp != 0 || !work || slot < 0) return;
@@ -776,7 +864,7 @@ __device__ void w2_phase(const GemvParams& p, int bx, int b, int g1x, u32x4 (*s_
 // rest do the W2 phase of a block, which waits for that block's count.
 // Workgroups are dispatched in index order, so every W13 workgroup is running
 // or finished before a W2 workgroup waits (and the wait is bounded).
-template <bool SW>
+template <bool SW, bool Q>
 __global__ void __launch_bounds__(kWaves * 64) decode_kernel(GemvParams p, int g1x, int g2x) {
   __shared__ u32x4 s_tile[kWaves][kTileU4];
   __shared__ int s_slot[16];
@@ -785,7 +873,7 @@ __global__ void __launch_bounds__(kWaves * 64) decode_kernel(GemvParams p, int g
   const int t = blockIdx.x;
   if (t < n1) {
     const int b = t / g1x;
-    w13_phase<SW>(p, t % g1x, b, s_tile, s_slot);
+    w13_phase<SW, Q>(p, t % g1x, b, s_tile, s_slot);
     // every thread's device-coherent act stores have completed before the count
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
@@ -793,7 +881,7 @@ __global__ void __launch_bounds__(kWaves * 64) decode_kernel(GemvParams p, int g
       __hip_atomic_fetch_add(&p.ctl[b * kCtlStride], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   } else {
     const int t2 = t - n1;
-    w2_phase(p, t2 % g2x, t2 / g2x, g1x, s_tile, s_slot);
+    w2_phase<Q>(p, t2 % g2x, t2 / g2x, g1x, s_tile, s_slot);
   }
 }
 
@@ -807,8 +895,8 @@ static int pick_tiles(int64_t tiles, int waves, int64_t target) {
   return nt;
 }
 
-hipError_t launch_gemv(const GemvParams& p0, bool swiglu, hipStream_t s) {
-  GemvParams p = p0;
+template <bool Q>
+static hipError_t launch_gemv_fmt(GemvParams p, bool swiglu, hipStream_t s) {
   const int nb = p.nblk + (p.sw13 ? 1 : 0);
   const int tiles1 = (p.I + 15) / 16;
   const int tiles2 = (p.H + 15) / 16;
@@ -822,19 +910,23 @@ hipError_t launch_gemv(const GemvParams& p0, bool swiglu, hipStream_t s) {
     hipLaunchKernelGGL(route_kernel, dim3(1), dim3(kRouteWaves * 64), 0, s, p);
     const unsigned nwg = (unsigned)((g1x + g2x) * nb);
     if (swiglu)
-      hipLaunchKernelGGL(decode_kernel<true>, dim3(nwg), dim3(kWaves * 64), 0, s, p, g1x, g2x);
+      hipLaunchKernelGGL((decode_kernel<true, Q>), dim3(nwg), dim3(kWaves * 64), 0, s, p, g1x, g2x);
     else
-      hipLaunchKernelGGL(decode_kernel<false>, dim3(nwg), dim3(kWaves * 64), 0, s, p, g1x, g2x);
+      hipLaunchKernelGGL((decode_kernel<false, Q>), dim3(nwg), dim3(kWaves * 64), 0, s, p, g1x, g2x);
     return hipGetLastError();
   }
   dim3 g1(g1x, nb);
   if (swiglu)
-    hipLaunchKernelGGL(gemv1_kernel<true>, g1, dim3(kG1Waves * 64), 0, s, p);
+    hipLaunchKernelGGL((gemv1_kernel<true, Q>), g1, dim3(kG1Waves * 64), 0, s, p);
   else
-    hipLaunchKernelGGL(gemv1_kernel<false>, g1, dim3(kG1Waves * 64), 0, s, p);
+    hipLaunchKernelGGL((gemv1_kernel<false, Q>), g1, dim3(kG1Waves * 64), 0, s, p);
   dim3 g2(g2x, nb);
-  hipLaunchKernelGGL(gemv2_kernel, g2, dim3(kG2Waves * 64), 0, s, p);
+  hipLaunchKernelGGL((gemv2_kernel<Q>), g2, dim3(kG2Waves * 64), 0, s, p);
   return hipGetLastError();
+}
+
+hipError_t launch_gemv(const GemvParams& p, bool swiglu, hipStream_t s) {
+  return p.mx ? launch_gemv_fmt<true>(p, swiglu, s) : launch_gemv_fmt<false>(p, swiglu, s);
 }
 
 }  // namespace moe

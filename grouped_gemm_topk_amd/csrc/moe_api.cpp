@@ -352,15 +352,29 @@ int moe_grouped_gemm_backward(const moe_gemm_backward_args* args, void* workspac
   return MOE_OK;
 }
 
-int moe_fused_forward(const moe_layer_params* p, const void* x, const float* router_logits,
-                      const void* w13, const void* w2, const void* shared_w13,
-                      const void* shared_w2, float* out, int32_t* topk_ids, float* topk_weights,
-                      int32_t* sorted_token_ids, int32_t* expert_ids,
-                      int32_t* num_tokens_post_padded, void* workspace, size_t* workspace_bytes,
-                      void* stream) {
+namespace {
+
+// MXFP8 weight scales (E8M0, one per 32 elements along a row); all null for
+// bf16 weights
+struct MxScales {
+  const uint8_t* w13;
+  const uint8_t* w2;
+  const uint8_t* sw13;
+  const uint8_t* sw2;
+};
+
+int fused_forward(const moe_layer_params* p, const void* x, const float* router_logits,
+                  const void* w13, const void* w2, const void* shared_w13, const void* shared_w2,
+                  const MxScales* mx, float* out, int32_t* topk_ids, float* topk_weights,
+                  int32_t* sorted_token_ids, int32_t* expert_ids, int32_t* num_tokens_post_padded,
+                  void* workspace, size_t* workspace_bytes, void* stream) {
   if (!workspace_bytes) return MOE_ERR_NULL;
   int st = validate_layer(p);
   if (st != MOE_OK) return st;
+  if (mx) {   // the MXFP8 form is the decode path: T <= 16, rows in blocks of 32
+    if (p->T > moe::kGemvMaxTokens) return MOE_ERR_UNSUPPORTED;
+    if (p->H % 32 != 0 || p->I % 32 != 0) return MOE_ERR_SHAPE;
+  }
   LayerWorkspace L = layout_layer(p, nullptr);
   if (!workspace) {
     *workspace_bytes = L.bytes;
@@ -370,6 +384,7 @@ int moe_fused_forward(const moe_layer_params* p, const void* x, const float* rou
   if (p->T == 0) return MOE_OK;
   if (!x || !router_logits || !w13 || !w2 || !out) return MOE_ERR_NULL;
   if (p->n_shared && (!shared_w13 || !shared_w2)) return MOE_ERR_NULL;
+  if (mx && (!mx->w13 || !mx->w2 || (p->n_shared && (!mx->sw13 || !mx->sw2)))) return MOE_ERR_NULL;
   if (!aligned16(x) || !aligned16(w13) || !aligned16(w2) || !aligned16(out) ||
       !aligned16(workspace) || !aligned4(router_logits) ||
       (p->n_shared && (!aligned16(shared_w13) || !aligned16(shared_w2))) ||
@@ -423,6 +438,13 @@ int moe_fused_forward(const moe_layer_params* p, const void* x, const float* rou
     gv.act_sh = L.act_sh;
     gv.out = out;
     gv.ctl = L.ctl;
+    if (mx) {
+      gv.mx = 1;
+      gv.w13_s = mx->w13;
+      gv.w2_s = mx->w2;
+      gv.sw13_s = p->n_shared ? mx->sw13 : nullptr;
+      gv.sw2_s = p->n_shared ? mx->sw2 : nullptr;
+    }
     return hip_status(moe::launch_gemv(gv, p->activation == MOE_ACT_SWIGLU, s));
   }
 
@@ -514,6 +536,33 @@ int moe_fused_forward(const moe_layer_params* p, const void* x, const float* rou
   // ---- combine
   e = moe::launch_combine(L.yslot, T, k, H, p->n_shared, out, s);
   return hip_status(e);
+}
+
+}  // namespace
+
+int moe_fused_forward(const moe_layer_params* p, const void* x, const float* router_logits,
+                      const void* w13, const void* w2, const void* shared_w13,
+                      const void* shared_w2, float* out, int32_t* topk_ids, float* topk_weights,
+                      int32_t* sorted_token_ids, int32_t* expert_ids,
+                      int32_t* num_tokens_post_padded, void* workspace, size_t* workspace_bytes,
+                      void* stream) {
+  return fused_forward(p, x, router_logits, w13, w2, shared_w13, shared_w2, nullptr, out,
+                       topk_ids, topk_weights, sorted_token_ids, expert_ids,
+                       num_tokens_post_padded, workspace, workspace_bytes, stream);
+}
+
+int moe_fused_forward_mxfp8(const moe_layer_params* p, const void* x, const float* router_logits,
+                            const void* w13_q, const uint8_t* w13_scale, const void* w2_q,
+                            const uint8_t* w2_scale, const void* shared_w13_q,
+                            const uint8_t* shared_w13_scale, const void* shared_w2_q,
+                            const uint8_t* shared_w2_scale, float* out, int32_t* topk_ids,
+                            float* topk_weights, int32_t* sorted_token_ids, int32_t* expert_ids,
+                            int32_t* num_tokens_post_padded, void* workspace,
+                            size_t* workspace_bytes, void* stream) {
+  const MxScales mx{w13_scale, w2_scale, shared_w13_scale, shared_w2_scale};
+  return fused_forward(p, x, router_logits, w13_q, w2_q, shared_w13_q, shared_w2_q, &mx, out,
+                       topk_ids, topk_weights, sorted_token_ids, expert_ids,
+                       num_tokens_post_padded, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -91,6 +91,13 @@ struct GemvParams {
   const uint16_t* w2;       // [E, H, I]
   const uint16_t* sw13;     // shared expert [M1, H] or null
   const uint16_t* sw2;      // shared expert [H, I] or null
+  // MXFP8 weights (mx = 1): the four matrices above hold FP8 E4M3 bytes and
+  // these their E8M0 scales, one per 32 elements along each row
+  int mx;
+  const uint8_t* w13_s;     // [E, M1, H / 32]
+  const uint8_t* w2_s;      // [E, H, I / 32]
+  const uint8_t* sw13_s;    // [M1, H / 32] or null
+  const uint8_t* sw2_s;     // [H, I / 32] or null
   // routing outputs: written by GEMV1's workgroup (0,0), read by GEMV2
   int* topk_ids;            // [T * k]
   float* topk_w;            // [T * k]

@@ -24,7 +24,7 @@ ACT_SWIGLU, ACT_RELU2 = 0, 1
 EPI_STORE, EPI_SWIGLU, EPI_RELU2, EPI_WEIGHTED_SCATTER = 0, 1, 2, 3
 
 EXPORTED = ("moe_align", "moe_grouped_gemm", "moe_grouped_gemm_backward", "moe_fused_forward",
-            "moe_align_capacity", "moe_status_string")
+            "moe_fused_forward_mxfp8", "moe_align_capacity", "moe_status_string")
 
 
 class MoeError(RuntimeError):
@@ -81,6 +81,10 @@ def lib() -> ctypes.CDLL:
         L.moe_fused_forward.argtypes = [ctypes.POINTER(MoeLayerParams), vp, vp, vp, vp, vp, vp,
                                         vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moe_fused_forward.restype = ctypes.c_int
+        L.moe_fused_forward_mxfp8.argtypes = [ctypes.POINTER(MoeLayerParams), vp, vp, vp, vp, vp,
+                                              vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                                              vp]
+        L.moe_fused_forward_mxfp8.restype = ctypes.c_int
         L.moe_align_capacity.argtypes = [i32, i32, i32, i32]
         L.moe_align_capacity.restype = ctypes.c_int64
         L.moe_status_string.argtypes = [ctypes.c_int]
@@ -329,19 +333,34 @@ def fused_workspace_bytes(p: LayerParams) -> int:
 class FusedLayer:
     """A ready-to-run moe_fused_forward call: checked tensors, outputs and the
     workspace are bound once, ``run()`` only enqueues the library call (the
-    form used for timing and graph capture)."""
+    form used for timing and graph capture).
+
+    With ``scales`` (a dict of uint8 tensors ``w13``, ``w2`` and, with a
+    shared expert, ``shared_w13``, ``shared_w2``: E8M0 bytes, one per 32
+    elements along each row) the weight tensors are MXFP8 (uint8 FP8 E4M3
+    bytes of the same shapes) and the call is moe_fused_forward_mxfp8."""
 
     def __init__(self, p: LayerParams, x, logits, w13, w2, shared_w13=None, shared_w2=None,
-                 out=None, routing_outputs: bool = False, workspace=None):
+                 out=None, routing_outputs: bool = False, workspace=None, scales=None):
         self.p = p
         dev = x.device
+        wt = torch.uint8 if scales is not None else torch.bfloat16
         _dev(x, "x", torch.bfloat16, (p.T, p.H))
         _dev(logits, "router_logits", torch.float32, (p.T, p.E))
-        _dev(w13, "w13", torch.bfloat16, (p.E, p.M1, p.H))
-        _dev(w2, "w2", torch.bfloat16, (p.E, p.H, p.I))
+        _dev(w13, "w13", wt, (p.E, p.M1, p.H))
+        _dev(w2, "w2", wt, (p.E, p.H, p.I))
         if p.n_shared:
-            _dev(shared_w13, "shared_w13", torch.bfloat16, (p.M1, p.H))
-            _dev(shared_w2, "shared_w2", torch.bfloat16, (p.H, p.I))
+            _dev(shared_w13, "shared_w13", wt, (p.M1, p.H))
+            _dev(shared_w2, "shared_w2", wt, (p.H, p.I))
+        self.scales = scales
+        if scales is not None:
+            if p.H % 32 or p.I % 32:
+                raise ValueError("MXFP8 weights need H and I multiples of 32")
+            _dev(scales["w13"], "w13 scales", torch.uint8, (p.E, p.M1, p.H // 32))
+            _dev(scales["w2"], "w2 scales", torch.uint8, (p.E, p.H, p.I // 32))
+            if p.n_shared:
+                _dev(scales["shared_w13"], "shared_w13 scales", torch.uint8, (p.M1, p.H // 32))
+                _dev(scales["shared_w2"], "shared_w2 scales", torch.uint8, (p.H, p.I // 32))
         if out is None:
             out = torch.empty((p.T, p.H), dtype=torch.float32, device=dev)
         _dev(out, "out", torch.float32, (p.T, p.H))
@@ -365,11 +384,20 @@ class FusedLayer:
         self._cp = p.c_struct()
         r = self.routing
         t = self.tensors
-        self._args = [ctypes.byref(self._cp), _ptr(t["x"]), _ptr(t["logits"]), _ptr(t["w13"]),
-                      _ptr(t["w2"]), _ptr(t["shared_w13"]), _ptr(t["shared_w2"]), _ptr(t["out"]),
-                      _ptr(r.get("topk_ids")), _ptr(r.get("topk_weights")),
-                      _ptr(r.get("sorted_token_ids")), _ptr(r.get("expert_ids")),
-                      _ptr(r.get("num_tokens_post_padded")), _ptr(workspace)]
+        tail = [_ptr(t["out"]), _ptr(r.get("topk_ids")), _ptr(r.get("topk_weights")),
+                _ptr(r.get("sorted_token_ids")), _ptr(r.get("expert_ids")),
+                _ptr(r.get("num_tokens_post_padded")), _ptr(workspace)]
+        if scales is None:
+            self._call = "moe_fused_forward"
+            self._args = [ctypes.byref(self._cp), _ptr(t["x"]), _ptr(t["logits"]), _ptr(t["w13"]),
+                          _ptr(t["w2"]), _ptr(t["shared_w13"]), _ptr(t["shared_w2"])] + tail
+        else:
+            self._call = "moe_fused_forward_mxfp8"
+            self._args = [ctypes.byref(self._cp), _ptr(t["x"]), _ptr(t["logits"]), _ptr(t["w13"]),
+                          _ptr(scales["w13"]), _ptr(t["w2"]), _ptr(scales["w2"]),
+                          _ptr(t["shared_w13"]), _ptr(scales.get("shared_w13")),
+                          _ptr(t["shared_w2"]), _ptr(scales.get("shared_w2"))] + tail
+        self._fn = getattr(lib(), self._call)
         self._n = ctypes.c_size_t(workspace.numel())
 
     @property
@@ -378,9 +406,24 @@ class FusedLayer:
 
     def run(self, stream=None) -> torch.Tensor:
         self._n.value = self.workspace.numel()
-        _check("moe_fused_forward", lib().moe_fused_forward(*self._args, ctypes.byref(self._n),
-                                                            _stream(stream)))
+        _check(self._call, self._fn(*self._args, ctypes.byref(self._n), _stream(stream)))
         return self.tensors["out"]
+
+
+def moe_fused_forward_mxfp8(p: LayerParams, x, router_logits, w13_q, w13_scale, w2_q, w2_scale,
+                            shared_w13_q=None, shared_w13_scale=None, shared_w2_q=None,
+                            shared_w2_scale=None, out=None, return_routing: bool = False,
+                            stream=None):
+    """The layer with MXFP8 expert weights (decode shapes, T <= 16): uint8 FP8
+    E4M3 weight bytes and uint8 E8M0 scales, one per 32 elements along a row."""
+    sc = {"w13": w13_scale, "w2": w2_scale}
+    if p.n_shared:
+        sc["shared_w13"], sc["shared_w2"] = shared_w13_scale, shared_w2_scale
+    layer = FusedLayer(p, x, router_logits, w13_q, w2_q, shared_w13_q, shared_w2_q, out,
+                       routing_outputs=return_routing, scales=sc)
+    if p.T > 0:
+        layer.run(stream)
+    return (layer.out, layer.routing) if return_routing else layer.out
 
 
 def moe_fused_forward(p: LayerParams, x, router_logits, w13, w2, shared_w13=None, shared_w2=None,

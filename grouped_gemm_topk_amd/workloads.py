@@ -320,15 +320,17 @@ def quantize_mxfp8(bits: np.ndarray):
     return q.view(torch.uint8).numpy().reshape(shp), sbits
 
 
-def make_mxfp8_weights(inp: Dict[str, np.ndarray]) -> Dict[str, np.ndarray]:
+def make_mxfp8_weights(inp: Dict[str, np.ndarray], experts=None) -> Dict[str, np.ndarray]:
     """MXFP8 forms of the layer's weights, expert by expert: w13_q / w13_s,
-    w2_q / w2_s and, with a shared expert, shared_w13_q / _s, shared_w2_q / _s."""
+    w2_q / w2_s and, with a shared expert, shared_w13_q / _s, shared_w2_q / _s.
+    ``experts``: convert only these (the others stay zero bytes), for timing
+    runs whose routing is known to read no other expert."""
     out: Dict[str, np.ndarray] = {}
     for name in ("w13", "w2"):
         w = inp[name]
-        q = np.empty(w.shape, dtype=np.uint8)
-        s = np.empty(w.shape[:-1] + (w.shape[-1] // MX_BLOCK,), dtype=np.uint8)
-        for e in range(w.shape[0]):
+        q = np.zeros(w.shape, dtype=np.uint8)
+        s = np.zeros(w.shape[:-1] + (w.shape[-1] // MX_BLOCK,), dtype=np.uint8)
+        for e in (range(w.shape[0]) if experts is None else experts):
             q[e], s[e] = quantize_mxfp8(w[e])
         out[name + "_q"], out[name + "_s"] = q, s
     for name in ("shared_w13", "shared_w2"):

@@ -233,6 +233,37 @@ int moe_fused_forward(const moe_layer_params* p, const void* x, const float* rou
                       int32_t* num_tokens_post_padded, void* workspace,
                       size_t* workspace_bytes, void* stream);
 
+/*
+ * The same layer with MXFP8 expert weights, for decode shapes (T <= 16), where
+ * the layer reads each touched expert's weights from HBM once and halving the
+ * bytes per weight halves that stream.  MXFP8 is the OCP Microscaling format:
+ * FP8 E4M3 elements (bias 7, no infinities, S.1111.111 = NaN) in blocks of 32
+ * consecutive elements along a row's contiguous dimension, each block with one
+ * E8M0 scale byte s meaning 2^(s - 127).  Element value = E4M3 value * 2^(s-127);
+ * the library decodes it exactly to bf16 (three mantissa bits times a power of
+ * two) and then computes exactly as moe_fused_forward does with those bf16
+ * weights.  Quantised weights for decode are a ranked next step of the
+ * axolotl page's grouped GEMM (its fp8 path is left unimplemented there) and
+ * of the B70 grouped-Q8 decode experiment (8-bit blocks).
+ *
+ *   w13_q [E, M1, H] bytes + w13_scale [E, M1, H / 32]
+ *   w2_q [E, H, I] bytes + w2_scale [E, H, I / 32]
+ *   shared_w13_q / _scale, shared_w2_q / _scale likewise (n_shared = 1), or NULL
+ * Everything else (routing, outputs, workspace and its size) as
+ * moe_fused_forward.  Extra limits: T <= 16 (MOE_ERR_UNSUPPORTED above), H and
+ * I multiples of 32 (MOE_ERR_SHAPE).  Scales must keep the decoded values
+ * inside bf16's normal range (s in [10, 246] for every block that has nonzero
+ * elements); E4M3 NaN codes give NaN.
+ */
+int moe_fused_forward_mxfp8(const moe_layer_params* p, const void* x, const float* router_logits,
+                            const void* w13_q, const uint8_t* w13_scale, const void* w2_q,
+                            const uint8_t* w2_scale, const void* shared_w13_q,
+                            const uint8_t* shared_w13_scale, const void* shared_w2_q,
+                            const uint8_t* shared_w2_scale, float* out, int32_t* topk_ids,
+                            float* topk_weights, int32_t* sorted_token_ids, int32_t* expert_ids,
+                            int32_t* num_tokens_post_padded, void* workspace,
+                            size_t* workspace_bytes, void* stream);
+
 /* Human-readable text of a status code (static storage). */
 const char* moe_status_string(int status);
 

@@ -196,3 +196,32 @@ def test_grouped_gemm_backward_validation_and_sizes(L):
     assert call(ws=fake, n=1 << 30, expert_ids=None)[0] == -1
     assert call(ws=fake + 8, n=1 << 30)[0] == -5
     assert L.moe_grouped_gemm_backward(None, None, None, None) == -1
+
+
+def test_fused_forward_mxfp8_validation(L):
+    """MXFP8 entry point: decode shapes only, rows in blocks of 32, scales
+    required; the workspace is the bf16 layer's."""
+    p = _layer(H=64, I=64).c_struct()
+    n = ctypes.c_size_t(0)
+    assert L.moe_fused_forward_mxfp8(ctypes.byref(p), *([None] * 17), ctypes.byref(n), None) == 0
+    nb = ctypes.c_size_t(0)
+    assert L.moe_fused_forward(ctypes.byref(p), *([None] * 13), ctypes.byref(nb), None) == 0
+    assert n.value == nb.value > 0
+    for kw, status in [(dict(T=17, H=64, I=64), -4), (dict(H=72, I=64), -2),
+                       (dict(H=64, I=40), -2)]:
+        q = _layer(**kw).c_struct()
+        m = ctypes.c_size_t(0)
+        assert L.moe_fused_forward_mxfp8(ctypes.byref(q), *([None] * 17), ctypes.byref(m),
+                                         None) == status
+    fake = 1 << 20
+    ok = ctypes.c_size_t(n.value)
+    args = [fake] * 17
+    args[3] = None   # w13 scales missing
+    assert L.moe_fused_forward_mxfp8(ctypes.byref(p), *args, ctypes.byref(ok), None) == -1
+    ps = _layer(H=64, I=64, n_shared=1).c_struct()
+    ns = ctypes.c_size_t(0)
+    L.moe_fused_forward_mxfp8(ctypes.byref(ps), *([None] * 17), ctypes.byref(ns), None)
+    for i in (7, 9):   # shared_w13 scales, shared_w2 scales missing
+        args = [fake] * 17
+        args[i] = None
+        assert L.moe_fused_forward_mxfp8(ctypes.byref(ps), *args, ctypes.byref(ns), None) == -1

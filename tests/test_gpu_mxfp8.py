@@ -1,0 +1,135 @@
+"""Parity of the MXFP8-weight decode layer (moe_fused_forward_mxfp8) against
+the oracle on the decoded weights.
+
+The library decodes every E4M3 element times its block's E8M0 scale exactly to
+bf16 and then computes as the bf16 layer does, so the bar is the bf16 layer's:
+routing bit-exact, output max|d| <= 2e-2 and relative-L2 <= 5e-3 against the
+oracle run on the weights the MXFP8 bytes represent.  Both decode forms are
+covered (below 48 slots GEMV1 + GEMV2, from 48 slots the fused launch).
+"""
+import numpy as np
+import pytest
+
+from grouped_gemm_topk_amd import workloads as W
+from oracle import moe_oracle as O
+from tests.helpers import to_dev
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def moe():
+    from grouped_gemm_topk_amd import moe as M
+    M.lib()
+    return M
+
+
+def _dev_u8(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _run(moe, cfg, inp, mx, routing=True):
+    p = moe.LayerParams.from_config(cfg)
+    sh = {}
+    if cfg.n_shared:
+        sh = dict(shared_w13_q=_dev_u8(mx["shared_w13_q"]), shared_w13_scale=_dev_u8(mx["shared_w13_s"]),
+                  shared_w2_q=_dev_u8(mx["shared_w2_q"]), shared_w2_scale=_dev_u8(mx["shared_w2_s"]))
+    out, r = moe.moe_fused_forward_mxfp8(p, to_dev(inp["x"]), to_dev(inp["logits"]),
+                                         _dev_u8(mx["w13_q"]), _dev_u8(mx["w13_s"]),
+                                         _dev_u8(mx["w2_q"]), _dev_u8(mx["w2_s"]),
+                                         return_routing=True, **sh)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), r
+
+
+def _check(cfg, inp, mx, got, r):
+    ref = O.moe_forward_mxfp8_cfg(cfg, inp, mx)
+    assert np.array_equal(r["topk_ids"].cpu().numpy(), ref["topk_ids"])
+    nt = int(r["num_tokens_post_padded"].cpu().item())
+    assert nt == ref["num_tokens_post_padded"]
+    assert np.array_equal(r["sorted_token_ids"].cpu().numpy()[:nt], ref["sorted_token_ids"])
+    want = ref["out"].astype(np.float64)
+    err = np.abs(got.astype(np.float64) - want)
+    rel = np.linalg.norm(got - want) / np.linalg.norm(want)
+    assert np.all(np.isfinite(got)), "output left unwritten"
+    assert err.max() <= 2e-2 and rel <= 5e-3, f"max|d|={err.max():.3g} rel-L2={rel:.3g}"
+
+
+SMALL = [
+    W.small_config("mx_t1", T=1, H=128, I=96, E=8, top_k=2),
+    W.small_config("mx_t3_e64", T=3, H=256, I=128, E=64, top_k=8),
+    W.small_config("mx_ragged_k", T=2, H=288, I=160, E=16, top_k=4),
+    W.small_config("mx_groups_shared", T=3, H=128, I=64, E=18, top_k=4, scoring=W.SCORE_SIGMOID,
+                   n_group=6, topk_group=4, n_shared=1, block_m=128),
+    # from 48 slots: the fused launch
+    W.small_config("mx_fused_t8", T=8, H=256, I=128, E=32, top_k=8),
+    W.small_config("mx_fused_shared", T=14, H=160, I=96, E=18, top_k=4, scoring=W.SCORE_SIGMOID,
+                   n_group=6, topk_group=4, n_shared=1, block_m=16),
+    W.small_config("mx_fused_relu2", T=16, H=128, I=64, E=32, top_k=6, activation=W.ACT_RELU2),
+]
+
+
+@pytest.mark.parametrize("cfg", SMALL, ids=[c.name for c in SMALL])
+def test_mxfp8_decode_small(moe, cfg):
+    print(f"mxfp8 decode {cfg.name}", flush=True)
+    inp = W.make_inputs(cfg)
+    mx = W.make_mxfp8_weights(inp)
+    got, r = _run(moe, cfg, inp, mx)
+    _check(cfg, inp, mx, got, r)
+
+
+FULL = ["decode_t1", "decode_t3", "decode_t8", "relu2_t1", "relu2_t16"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_mxfp8_decode_full_size(moe, name):
+    print(f"mxfp8 decode full size {name}", flush=True)
+    cfg = W.CONFIGS[name]
+    inp = W.make_inputs(cfg)
+    mx = W.make_mxfp8_weights(inp)
+    got, r = _run(moe, cfg, inp, mx)
+    _check(cfg, inp, mx, got, r)
+
+
+def test_mxfp8_rejects_prefill_shapes(moe):
+    cfg = W.small_config("mx_prefill", T=17, H=64, I=64, E=8, top_k=2)
+    inp = W.make_inputs(cfg)
+    mx = W.make_mxfp8_weights(inp)
+    with pytest.raises(moe.MoeError) as ei:
+        _run(moe, cfg, inp, mx)
+    assert ei.value.status == -4
+
+
+def test_mxfp8_graph_replays(moe):
+    """The fused MXFP8 launch captured once and replayed with eager work in
+    between; every replay within fp32 reassociation of the eager result."""
+    cfg = W.small_config("mx_graph", T=8, H=256, I=128, E=32, top_k=8)
+    inp = W.make_inputs(cfg)
+    mx = W.make_mxfp8_weights(inp)
+    p = moe.LayerParams.from_config(cfg)
+    layer = moe.FusedLayer(p, to_dev(inp["x"]), to_dev(inp["logits"]), _dev_u8(mx["w13_q"]),
+                           _dev_u8(mx["w2_q"]),
+                           scales={"w13": _dev_u8(mx["w13_s"]), "w2": _dev_u8(mx["w2_s"])})
+    eager = layer.run().clone()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layer.run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        out = layer.run()
+    torch.cuda.synchronize()
+    want = eager.cpu().numpy()
+    for rep in range(3):
+        layer.tensors["out"].fill_(float("nan"))
+        if rep == 1:
+            layer.run()
+        g.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_allclose(out.cpu().numpy(), want, rtol=1e-5,
+                                   atol=1e-6 * np.abs(want).max(), err_msg=f"replay {rep}")
