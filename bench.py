@@ -13,7 +13,8 @@ with HIP events on its stream), decode microseconds per layer at T = 1, 3, 8
 through enough distinct layers that the 256 MB Infinity Cache cannot hold the
 touched weights and cross-checked with an explicit cache flush before every
 call, the standalone grouped GEMM at the four shapes of the axolotl page's
-benchmark table, the achievable peaks of this GPU from the probe library's own MFMA-loop
+benchmark table, the layer with the router logits fused into gating against a
+separate router GEMM, the achievable peaks of this GPU from the probe library's own MFMA-loop
 and streaming-read kernels, and the CPU oracle's rate on a bounded sample of
 the same workload.
 """
@@ -65,6 +66,9 @@ def parse():
     ap.add_argument("--no-peaks", action="store_true", help="skip the achievable-peak probes")
     ap.add_argument("--no-gemm-scenarios", action="store_true",
                     help="skip the standalone grouped-GEMM scenarios")
+    ap.add_argument("--no-router", action="store_true", help="skip the router-fusion comparison")
+    ap.add_argument("--router-only", action="store_true",
+                    help="only the router-fusion comparison (one JSON line)")
     ap.add_argument("--gemm-scenarios-only", action="store_true",
                     help="only the standalone grouped-GEMM scenarios (one JSON line), for profiler passes")
     ap.add_argument("--cpu-tokens", type=int, default=4096,
@@ -388,6 +392,58 @@ def gemm_scenarios(steps, warmup, torch, moe, W):
     return res
 
 
+def router_cases(steps, warmup, torch, moe, W):
+    """The layer from the hidden states and the router weight: the router's
+    linear layer fused into gating (moe_fused_forward_router) against the
+    separate pipeline (an fp32 torch.matmul for the logits, as the HF gate
+    computes them, then moe_fused_forward).  Prefill: eager calls in
+    alternation; decode: graph replays of one call each (weights stay in the
+    caches, the same for both)."""
+    res = []
+    for name in ("dsv3", "decode_t1"):
+        cfg = W.CONFIGS[name]
+        inp = W.make_inputs(cfg)
+        p = moe.LayerParams.from_config(cfg)
+        x = _to_dev(inp["x"], torch)
+        wr = _to_dev(W.make_router_weight(cfg), torch)
+        w = {k: _to_dev(inp[k], torch) for k in ("w13", "w2", "shared_w13", "shared_w2") if k in inp}
+        sh = (w.get("shared_w13"), w.get("shared_w2"))
+        fused = moe.FusedLayer(p, x, None, w["w13"], w["w2"], *sh, router_w=wr)
+        logits = torch.empty((cfg.T, cfg.E), dtype=torch.float32, device="cuda")
+        layer = moe.FusedLayer(p, x, logits, w["w13"], w["w2"], *sh)
+        xf, wrt = x.float(), wr.float().t().contiguous()
+
+        def separate():
+            torch.matmul(xf, wrt, out=logits)
+            layer.run()
+        if cfg.T > 16:
+            ms_f, ms_s = _interleaved_ms([fused.run, separate], steps, warmup, torch)
+        else:
+            ms_f, ms_s = [_graph_replay_ms(f, steps, warmup, torch) for f in (fused.run, separate)]
+        res.append({"config": name, "fused_router_ms": round(ms_f, 4),
+                    "separate_router_ms": round(ms_s, 4),
+                    "timing": "eager, alternating" if cfg.T > 16 else "graph replays, warm caches"})
+        del fused, layer, w, x, wr, xf, wrt, logits
+        torch.cuda.empty_cache()
+    return res
+
+
+def _graph_replay_ms(fn, steps, warmup, torch):
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(10):
+            fn()
+    ms = _event_ms(g.replay, max(1, steps // 10), max(1, warmup // 10), torch) / 10
+    del g
+    return ms
+
+
 def achievable_peaks(torch, reps=5):
     """This GPU's achievable rates from the probe library (libmoe_probe.so,
     built beside libmoe.so): dense bf16 MFMA TFLOP/s of a loop of independent
@@ -505,6 +561,10 @@ def main():
         copy_calibration(torch)
         return
     moe.lib()
+    if args.router_only:
+        print(json.dumps({"router_fused": router_cases(args.steps, args.warmup, torch, moe, W)}),
+              flush=True)
+        return
     if args.gemm_scenarios_only:
         print(json.dumps({"grouped_gemm_scenarios": gemm_scenarios(args.steps, args.warmup, torch,
                                                                    moe, W)}), flush=True)
@@ -568,6 +628,8 @@ def main():
                 d["frac_of_achievable_hbm"] = round(d["GBps"] / peaks["hbm_read_GBps"], 4)
     if not args.no_gemm_scenarios:
         line["grouped_gemm_scenarios"] = gemm_scenarios(args.steps, args.warmup, torch, moe, W)
+    if not args.no_router:
+        line["router_fused"] = router_cases(args.steps, args.warmup, torch, moe, W)
     extra = [e for e in args.extra.split(",") if e]
     if extra:
         line["extra"] = {}

@@ -105,6 +105,7 @@ struct LayerWorkspace {
   uint16_t* act;      // [cap, I] bf16 in padded order
   uint16_t* act_sh;   // [T, I] bf16, shared expert
   int32_t* ctl;       // decode kernel's control block
+  float* logits;      // [T, E] router logits computed by the library (router path)
   float* yslot;       // [T*k (+T), H] fp32 weighted expert outputs
   size_t bytes;
 };
@@ -124,6 +125,7 @@ LayerWorkspace layout_layer(const moe_layer_params* p, void* ws) {
   w.act_sh = (uint16_t*)c.take((size_t)(p->n_shared ? p->T : 0) * p->I * 2);
   w.yslot = (float*)c.take((size_t)(n + (p->n_shared ? p->T : 0)) * p->H * 4);
   w.ctl = (int32_t*)c.take((size_t)(moe::kMaxExperts + 1) * 32 * sizeof(int32_t));
+  w.logits = (float*)c.take((size_t)p->T * p->E * sizeof(float));
   w.bytes = c.off;
   return w;
 }
@@ -363,9 +365,14 @@ struct MxScales {
   const uint8_t* sw2;
 };
 
+// router_w non-null: the router logits are computed here (x . router_w^T) into
+// router_logits (an output then, or the workspace when null) together with
+// the gating
 int fused_forward(const moe_layer_params* p, const void* x, const float* router_logits,
-                  const void* w13, const void* w2, const void* shared_w13, const void* shared_w2,
-                  const MxScales* mx, float* out, int32_t* topk_ids, float* topk_weights,
+                  bool router, const void* router_w, const void* w13, const void* w2,
+                  const void* shared_w13,
+                  const void* shared_w2, const MxScales* mx, float* out, int32_t* topk_ids,
+                  float* topk_weights,
                   int32_t* sorted_token_ids, int32_t* expert_ids, int32_t* num_tokens_post_padded,
                   void* workspace, size_t* workspace_bytes, void* stream) {
   if (!workspace_bytes) return MOE_ERR_NULL;
@@ -382,7 +389,8 @@ int fused_forward(const moe_layer_params* p, const void* x, const float* router_
   }
   if (*workspace_bytes < L.bytes) return MOE_ERR_CAPACITY;
   if (p->T == 0) return MOE_OK;
-  if (!x || !router_logits || !w13 || !w2 || !out) return MOE_ERR_NULL;
+  if (!x || !(router ? router_w : router_logits) || !w13 || !w2 || !out) return MOE_ERR_NULL;
+  if (router && !aligned16(router_w)) return MOE_ERR_ALIGN;
   if (p->n_shared && (!shared_w13 || !shared_w2)) return MOE_ERR_NULL;
   if (mx && (!mx->w13 || !mx->w2 || (p->n_shared && (!mx->sw13 || !mx->sw2)))) return MOE_ERR_NULL;
   if (!aligned16(x) || !aligned16(w13) || !aligned16(w2) || !aligned16(out) ||
@@ -407,12 +415,34 @@ int fused_forward(const moe_layer_params* p, const void* x, const float* router_
   int32_t* eids = expert_ids ? expert_ids : L.expert_ids;
   int32_t* ntpp = num_tokens_post_padded ? num_tokens_post_padded : L.ntpp;
 
+  // ---- router path: logits and gating in one launch
+  const float* logits = router_logits;
+  if (router) {
+    float* lg = router_logits ? (float*)router_logits : L.logits;
+    moe::GateParams g{};
+    g.T = T;
+    g.E = E;
+    g.k = k;
+    g.scoring = p->scoring;
+    g.n_group = p->n_group;
+    g.topk_group = p->topk_group;
+    g.renorm = p->renormalize;
+    g.scale = p->routed_scaling_factor;
+    g.topk_ids = ids;
+    g.topk_w = wts;
+    // decode shapes gate in their GEMV path; otherwise gating rides along
+    hipError_t e = moe::launch_router(g, (const uint16_t*)x, (const uint16_t*)router_w, H, lg,
+                                      T > moe::kGemvMaxTokens, s);
+    if (e != hipSuccess) return hip_status(e);
+    logits = lg;
+  }
+
   // ---- decode shapes: routing folded into the first of two expert GEMVs,
   // each touched expert's weights read once
   if (T <= moe::kGemvMaxTokens) {
     moe::GemvParams gv{};
     gv.x = (const uint16_t*)x;
-    gv.logits = router_logits;
+    gv.logits = logits;
     gv.w13 = (const uint16_t*)w13;
     gv.w2 = (const uint16_t*)w2;
     gv.sw13 = p->n_shared ? (const uint16_t*)shared_w13 : nullptr;
@@ -450,7 +480,7 @@ int fused_forward(const moe_layer_params* p, const void* x, const float* router_
 
   // ---- routing
   moe::GateParams g{};
-  g.logits = router_logits;
+  g.logits = logits;
   g.T = T;
   g.E = E;
   g.k = k;
@@ -463,7 +493,9 @@ int fused_forward(const moe_layer_params* p, const void* x, const float* router_
   g.topk_w = wts;
   moe::AlignParams a = make_align(ids, n, E, bm, sorted, eids, ntpp, L.align_scratch);
   hipError_t e;
-  if (T <= moe::kRouteFusedTokens && n <= moe::kSingleBlockSlots) {
+  if (router) {   // gating done with the logits: align only
+    e = moe::launch_align(a, s);
+  } else if (T <= moe::kRouteFusedTokens && n <= moe::kSingleBlockSlots) {
     e = moe::launch_route_fused(g, a, s);
   } else {
     e = moe::launch_gate(g, s);
@@ -546,8 +578,19 @@ int moe_fused_forward(const moe_layer_params* p, const void* x, const float* rou
                       int32_t* sorted_token_ids, int32_t* expert_ids,
                       int32_t* num_tokens_post_padded, void* workspace, size_t* workspace_bytes,
                       void* stream) {
-  return fused_forward(p, x, router_logits, w13, w2, shared_w13, shared_w2, nullptr, out,
-                       topk_ids, topk_weights, sorted_token_ids, expert_ids,
+  return fused_forward(p, x, router_logits, false, nullptr, w13, w2, shared_w13, shared_w2, nullptr,
+                       out, topk_ids, topk_weights, sorted_token_ids, expert_ids,
+                       num_tokens_post_padded, workspace, workspace_bytes, stream);
+}
+
+int moe_fused_forward_router(const moe_layer_params* p, const void* x, const void* router_w,
+                             float* router_logits_out, const void* w13, const void* w2,
+                             const void* shared_w13, const void* shared_w2, float* out,
+                             int32_t* topk_ids, float* topk_weights, int32_t* sorted_token_ids,
+                             int32_t* expert_ids, int32_t* num_tokens_post_padded,
+                             void* workspace, size_t* workspace_bytes, void* stream) {
+  return fused_forward(p, x, router_logits_out, true, router_w, w13, w2, shared_w13, shared_w2,
+                       nullptr, out, topk_ids, topk_weights, sorted_token_ids, expert_ids,
                        num_tokens_post_padded, workspace, workspace_bytes, stream);
 }
 
@@ -560,8 +603,8 @@ int moe_fused_forward_mxfp8(const moe_layer_params* p, const void* x, const floa
                             int32_t* num_tokens_post_padded, void* workspace,
                             size_t* workspace_bytes, void* stream) {
   const MxScales mx{w13_scale, w2_scale, shared_w13_scale, shared_w2_scale};
-  return fused_forward(p, x, router_logits, w13_q, w2_q, shared_w13_q, shared_w2_q, &mx, out,
-                       topk_ids, topk_weights, sorted_token_ids, expert_ids,
+  return fused_forward(p, x, router_logits, false, nullptr, w13_q, w2_q, shared_w13_q, shared_w2_q,
+                       &mx, out, topk_ids, topk_weights, sorted_token_ids, expert_ids,
                        num_tokens_post_padded, workspace, workspace_bytes, stream);
 }
 

@@ -119,6 +119,10 @@ hipError_t launch_gemv(const GemvParams& p, bool swiglu, hipStream_t s);
 
 hipError_t launch_gate(const GateParams& p, hipStream_t s);
 hipError_t launch_route_fused(const GateParams& g, const AlignParams& a, hipStream_t s);
+// logits = x . router_w^T (written to `logits`, [T, E] fp32); with `gate`
+// also the gating of every token (g.topk_ids / g.topk_w); g.logits is ignored
+hipError_t launch_router(const GateParams& g, const uint16_t* x, const uint16_t* router_w, int H,
+                         float* logits, bool gate, hipStream_t s);
 hipError_t launch_align(const AlignParams& p, hipStream_t s);
 hipError_t launch_grouped_gemm(const GemmParams& p, int block_m, hipStream_t s);
 // bf16 [B, R, C] -> [B, C, R] (R and C multiples of 8)

@@ -289,6 +289,155 @@ __global__ void __launch_bounds__(256) gate_kernel(GateParams p) {
   }
 }
 
+// Router logits x[t] . W_router[e] (fp32 accumulation, v_mfma_f32_16x16x32_bf16
+// with operands straight from L2, 16 experts x 16 tokens per tile).  Each
+// workgroup (16 waves) takes kRouterTokens tokens and either every expert
+// (GATE: the logits stay in LDS and each wave gates one token there) or one
+// tile of 16 experts (grid y; logits only, for decode, whose GEMV path
+// gates).  A wave accumulates up to kTiles expert tiles at once, so each
+// token fragment it loads serves all of them; the waves split H in 32-element
+// steps as many ways (ksplit) as the tile groups leave room for, and the
+// partial tiles are added in LDS in a fixed order.  LDS (dynamic, sized by E
+// on the host): region A = the partial tiles [ksplit][16][E16], reused after
+// the sum as per-wave gating scratch; then, for GATE, the logits [16][E].
+// The static allocation covers the largest E.
+constexpr int kRouterTokens = 16;
+typedef __bf16 rbf16x8 __attribute__((ext_vector_type(8)));
+typedef float rf32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned ru32x4 __attribute__((ext_vector_type(4)));
+
+template <bool GATE>
+struct RouterShape {
+  static constexpr int kWaves = 16;
+  static constexpr int kTiles = GATE ? 4 : 1;   // expert tiles one wave accumulates
+  static constexpr int kSteps = GATE ? 4 : 2;   // K steps whose loads are issued together
+  static constexpr int kLds = GATE ? 81920 : 16384;   // >= router_lds_bytes(E) for every E <= 256
+};
+
+struct RouterSplit {
+  int ntiles, ksplit, e16;
+};
+
+__host__ __device__ inline RouterSplit router_split(int E, bool gate) {
+  const int nw = gate ? RouterShape<true>::kWaves : RouterShape<false>::kWaves;
+  const int tpw = gate ? RouterShape<true>::kTiles : RouterShape<false>::kTiles;
+  RouterSplit r;
+  r.ntiles = gate ? (E + 15) / 16 : 1;
+  const int ngroups = (r.ntiles + tpw - 1) / tpw;
+  r.ksplit = nw / ngroups > 1 ? nw / ngroups : 1;
+  r.e16 = 16 * r.ntiles;
+  return r;
+}
+
+__host__ __device__ inline size_t router_region_a(int E, bool gate) {
+  const RouterSplit sp = router_split(E, gate);
+  size_t a = (size_t)sp.ksplit * kRouterTokens * sp.e16 * sizeof(float);
+  if (gate) {
+    const size_t scratch =
+        (size_t)RouterShape<true>::kWaves * (kMaxExperts * sizeof(double) + 64 * sizeof(int));
+    a = a > scratch ? a : scratch;
+  }
+  return (a + 15) / 16 * 16;
+}
+
+__host__ __device__ inline size_t router_lds_bytes(int E, bool gate) {
+  return router_region_a(E, gate) + (gate ? (size_t)kRouterTokens * E * sizeof(float) : 0);
+}
+
+template <bool GATE>
+__global__ void __launch_bounds__(RouterShape<GATE>::kWaves * 64) router_kernel(
+    GateParams g, const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, int H,
+    float* __restrict__ logits) {
+  constexpr int NW = RouterShape<GATE>::kWaves;
+  constexpr int TPW = RouterShape<GATE>::kTiles;
+  constexpr int U = RouterShape<GATE>::kSteps;
+  __shared__ __attribute__((aligned(16))) unsigned char router_lds[RouterShape<GATE>::kLds];
+  const RouterSplit sp = router_split(g.E, GATE);
+  float* s_part = (float*)router_lds;                                        // [ksplit][16][e16]
+  float* s_log = (float*)(router_lds + router_region_a(g.E, GATE));          // [16][E]
+  double* s_sig = (double*)router_lds;                                       // [NW][256] after the sum
+  int* s_keep = (int*)(s_sig + NW * kMaxExperts);                            // [NW][64]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int t0 = blockIdx.x * kRouterTokens;
+  const int nt = min(kRouterTokens, g.T - t0);
+  const int e_base = GATE ? 0 : blockIdx.y * 16;
+  const int kp = wave % sp.ksplit, tg = wave / sp.ksplit;
+  const int r = lane & 15, gq = lane >> 4;   // operand row / column r, K group gq
+  const uint16_t* xr = r < nt ? x + (int64_t)(t0 + r) * H : nullptr;
+  const ru32x4 zero = {0u, 0u, 0u, 0u};
+  auto ld = [&](const uint16_t* row, int kc) -> ru32x4 {
+    return (row && kc < H) ? *(const ru32x4*)(row + kc) : zero;
+  };
+  auto mma = [&](ru32x4 a, ru32x4 b, rf32x4 c) -> rf32x4 {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(rbf16x8, a),
+                                                   __builtin_bit_cast(rbf16x8, b), c, 0, 0, 0);
+  };
+  // tile group tg: tiles tg * TPW + j that exist.  The loop runs over
+  // groups of U K steps (32 elements each), every load of a group issued
+  // before its MFMAs; the trip count is wave-uniform (the MFMAs need the whole
+  // wave); each lane reads its 8 K elements from kb (H is a multiple of 8;
+  // zeros past H, so steps past the end add nothing)
+  const int tile0 = tg * TPW;
+  if (tile0 < sp.ntiles) {
+    const uint16_t* wrow[TPW];
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+      const int e = e_base + (tile0 + j) * 16 + r;
+      wrow[j] = (tile0 + j < sp.ntiles && e < g.E) ? wr + (int64_t)e * H : nullptr;
+    }
+    rf32x4 acc[TPW];
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) acc[j] = rf32x4{0.f, 0.f, 0.f, 0.f};
+    const int KS = 32 * sp.ksplit;
+    for (int kb = 32 * kp + 8 * gq; kb - 8 * gq < H; kb += U * KS) {
+      ru32x4 b[U], a[U][TPW];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        b[u] = ld(xr, kb + u * KS);
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) a[u][j] = ld(wrow[j], kb + u * KS);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) acc[j] = mma(a[u][j], b[u], acc[j]);
+    }
+    // lane (r, gq) holds experts 16 i + 4 gq + v of token r
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+      if (tile0 + j >= sp.ntiles) break;
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        s_part[(kp * kRouterTokens + r) * sp.e16 + (tile0 + j) * 16 + 4 * gq + v] = acc[j][v];
+    }
+  }
+  __syncthreads();
+  const int ne = GATE ? g.E : min(16, g.E - e_base);
+  for (int idx = tid; idx < nt * ne; idx += blockDim.x) {
+    const int t = idx / ne, j = idx - t * ne;
+    float v = 0.f;
+    for (int q = 0; q < sp.ksplit; ++q) v += s_part[(q * kRouterTokens + t) * sp.e16 + j];
+    logits[(int64_t)(t0 + t) * g.E + e_base + j] = v;
+    if (GATE) s_log[t * g.E + j] = v;
+  }
+  if (!GATE) return;
+  __syncthreads();   // region A becomes the gating scratch
+  GateParams lg = g;
+  lg.logits = s_log;   // the tile's logits, row stride E, in LDS
+  for (int t = wave; t < nt; t += NW) {
+    int id;
+    float w;
+    gate_token(lg, t, s_sig + wave * kMaxExperts, s_keep + wave * 64, &id, &w);
+    if (lane < g.k) {
+      g.topk_ids[(int64_t)(t0 + t) * g.k + lane] = id;
+      g.topk_w[(int64_t)(t0 + t) * g.k + lane] = w;
+    }
+  }
+}
+
 // One workgroup: all n <= kSingleBlockSlots slots.  When `do_gate` is set,
 // gating runs first inside the same workgroup (one wave per token).
 __global__ void __launch_bounds__(1024) align_single_kernel(AlignParams a, GateParams g,
@@ -406,6 +555,22 @@ hipError_t launch_gate(const GateParams& p, hipStream_t s) {
   if (p.T == 0) return hipSuccess;
   dim3 grid((p.T + 3) / 4);
   hipLaunchKernelGGL(gate_kernel, grid, dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_router(const GateParams& g, const uint16_t* x, const uint16_t* router_w, int H,
+                         float* logits, bool gate, hipStream_t s) {
+  if (g.T == 0) return hipSuccess;
+  const unsigned nb = (unsigned)((g.T + kRouterTokens - 1) / kRouterTokens);
+  if (g.E < 1 || g.E > kMaxExperts ||
+      router_lds_bytes(g.E, gate) > (size_t)(gate ? RouterShape<true>::kLds : RouterShape<false>::kLds))
+    return hipErrorInvalidValue;
+  if (gate)
+    hipLaunchKernelGGL(router_kernel<true>, dim3(nb), dim3(RouterShape<true>::kWaves * 64), 0, s, g,
+                       x, router_w, H, logits);
+  else
+    hipLaunchKernelGGL(router_kernel<false>, dim3(nb, (g.E + 15) / 16),
+                       dim3(RouterShape<false>::kWaves * 64), 0, s, g, x, router_w, H, logits);
   return hipGetLastError();
 }
 

@@ -24,7 +24,8 @@ ACT_SWIGLU, ACT_RELU2 = 0, 1
 EPI_STORE, EPI_SWIGLU, EPI_RELU2, EPI_WEIGHTED_SCATTER = 0, 1, 2, 3
 
 EXPORTED = ("moe_align", "moe_grouped_gemm", "moe_grouped_gemm_backward", "moe_fused_forward",
-            "moe_fused_forward_mxfp8", "moe_align_capacity", "moe_status_string")
+            "moe_fused_forward_mxfp8", "moe_fused_forward_router", "moe_align_capacity",
+            "moe_status_string")
 
 
 class MoeError(RuntimeError):
@@ -85,6 +86,9 @@ def lib() -> ctypes.CDLL:
                                               vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                               vp]
         L.moe_fused_forward_mxfp8.restype = ctypes.c_int
+        L.moe_fused_forward_router.argtypes = [ctypes.POINTER(MoeLayerParams), vp, vp, vp, vp, vp,
+                                               vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_fused_forward_router.restype = ctypes.c_int
         L.moe_align_capacity.argtypes = [i32, i32, i32, i32]
         L.moe_align_capacity.restype = ctypes.c_int64
         L.moe_status_string.argtypes = [ctypes.c_int]
@@ -335,17 +339,27 @@ class FusedLayer:
     workspace are bound once, ``run()`` only enqueues the library call (the
     form used for timing and graph capture).
 
+    With ``router_w`` (bf16 [E, H]) the router logits are computed by the
+    library (moe_fused_forward_router) into ``logits`` (allocated when None).
+
     With ``scales`` (a dict of uint8 tensors ``w13``, ``w2`` and, with a
     shared expert, ``shared_w13``, ``shared_w2``: E8M0 bytes, one per 32
     elements along each row) the weight tensors are MXFP8 (uint8 FP8 E4M3
     bytes of the same shapes) and the call is moe_fused_forward_mxfp8."""
 
     def __init__(self, p: LayerParams, x, logits, w13, w2, shared_w13=None, shared_w2=None,
-                 out=None, routing_outputs: bool = False, workspace=None, scales=None):
+                 out=None, routing_outputs: bool = False, workspace=None, scales=None,
+                 router_w=None):
         self.p = p
         dev = x.device
         wt = torch.uint8 if scales is not None else torch.bfloat16
         _dev(x, "x", torch.bfloat16, (p.T, p.H))
+        if router_w is not None:
+            if scales is not None:
+                raise ValueError("the router path takes bf16 expert weights")
+            _dev(router_w, "router_w", torch.bfloat16, (p.E, p.H))
+            if logits is None:
+                logits = torch.empty((p.T, p.E), dtype=torch.float32, device=dev)
         _dev(logits, "router_logits", torch.float32, (p.T, p.E))
         _dev(w13, "w13", wt, (p.E, p.M1, p.H))
         _dev(w2, "w2", wt, (p.E, p.H, p.I))
@@ -387,7 +401,13 @@ class FusedLayer:
         tail = [_ptr(t["out"]), _ptr(r.get("topk_ids")), _ptr(r.get("topk_weights")),
                 _ptr(r.get("sorted_token_ids")), _ptr(r.get("expert_ids")),
                 _ptr(r.get("num_tokens_post_padded")), _ptr(workspace)]
-        if scales is None:
+        if router_w is not None:
+            self._call = "moe_fused_forward_router"
+            self.tensors["router_w"] = router_w
+            self._args = [ctypes.byref(self._cp), _ptr(t["x"]), _ptr(router_w), _ptr(t["logits"]),
+                          _ptr(t["w13"]), _ptr(t["w2"]), _ptr(t["shared_w13"]),
+                          _ptr(t["shared_w2"])] + tail
+        elif scales is None:
             self._call = "moe_fused_forward"
             self._args = [ctypes.byref(self._cp), _ptr(t["x"]), _ptr(t["logits"]), _ptr(t["w13"]),
                           _ptr(t["w2"]), _ptr(t["shared_w13"]), _ptr(t["shared_w2"])] + tail
@@ -424,6 +444,19 @@ def moe_fused_forward_mxfp8(p: LayerParams, x, router_logits, w13_q, w13_scale, 
     if p.T > 0:
         layer.run(stream)
     return (layer.out, layer.routing) if return_routing else layer.out
+
+
+def moe_fused_forward_router(p: LayerParams, x, router_w, w13, w2, shared_w13=None,
+                             shared_w2=None, out=None, return_routing: bool = False, stream=None):
+    """The layer from the hidden states and the router weight: returns ``out``
+    (or ``(out, routing_dict)`` with the computed ``router_logits`` in it)."""
+    layer = FusedLayer(p, x, None, w13, w2, shared_w13, shared_w2, out,
+                       routing_outputs=return_routing, router_w=router_w)
+    if p.T > 0:
+        layer.run(stream)
+    if return_routing:
+        return layer.out, {**layer.routing, "router_logits": layer.tensors["logits"]}
+    return layer.out
 
 
 def moe_fused_forward(p: LayerParams, x, router_logits, w13, w2, shared_w13=None, shared_w2=None,

@@ -33,6 +33,7 @@ import numpy as np
 
 # tensor ids used in the seed keys
 _TID_X, _TID_LOGITS, _TID_W13, _TID_W2, _TID_SW13, _TID_SW2, _TID_PERM = 1, 2, 3, 4, 5, 6, 7
+_TID_ROUTER = 8
 
 SCORE_SOFTMAX, SCORE_SIGMOID = 0, 1
 ACT_SWIGLU, ACT_RELU2 = 0, 1
@@ -337,3 +338,13 @@ def make_mxfp8_weights(inp: Dict[str, np.ndarray], experts=None) -> Dict[str, np
         if name in inp:
             out[name + "_q"], out[name + "_s"] = quantize_mxfp8(inp[name])
     return out
+
+
+# ---------------------------------------------------------------------------
+# router weight (the gate's linear layer): for the path that computes the
+# router logits itself
+# ---------------------------------------------------------------------------
+def make_router_weight(cfg: MoEConfig, layer: int = 0) -> np.ndarray:
+    """bf16 bits [E, H] ~ N(0, w_std): the gate's weight, logits = x . W^T
+    (the HF DeepSeek-V3 gate's linear layer, ``initializer_range``)."""
+    return _normal_bf16((cfg.E, cfg.H), cfg.w_std, cfg.family, layer, _TID_ROUTER)

@@ -234,6 +234,27 @@ int moe_fused_forward(const moe_layer_params* p, const void* x, const float* rou
                       size_t* workspace_bytes, void* stream);
 
 /*
+ * The same layer with the router's linear layer fused into gating: the router
+ * logits x . router_w^T (the HF gate the axolotl benchmark calls on the hidden
+ * states, before the top-k) are formed with bf16 MFMAs and fp32 accumulation,
+ * 16 tokens per workgroup.  For T > 16 the gating launch forms them, keeps
+ * them on chip for the top-k and writes them out; for T <= 16 one small launch
+ * (16 experts per workgroup) writes them and the decode path gates them as
+ * moe_fused_forward does.  They go to router_logits_out ([T, E] fp32) when it
+ * is not NULL, else to the workspace.  The routing is decided on those fp32
+ * logits exactly as moe_fused_forward decides it on given logits.
+ *   router_w [E, H] bf16, 16-byte aligned; everything else as moe_fused_forward
+ * (same workspace size).  Errors: router_w NULL (MOE_ERR_NULL) or misaligned
+ * (MOE_ERR_ALIGN), then as moe_fused_forward.
+ */
+int moe_fused_forward_router(const moe_layer_params* p, const void* x, const void* router_w,
+                             float* router_logits_out, const void* w13, const void* w2,
+                             const void* shared_w13, const void* shared_w2, float* out,
+                             int32_t* topk_ids, float* topk_weights, int32_t* sorted_token_ids,
+                             int32_t* expert_ids, int32_t* num_tokens_post_padded,
+                             void* workspace, size_t* workspace_bytes, void* stream);
+
+/*
  * The same layer with MXFP8 expert weights, for decode shapes (T <= 16), where
  * the layer reads each touched expert's weights from HBM once and halving the
  * bytes per weight halves that stream.  MXFP8 is the OCP Microscaling format:

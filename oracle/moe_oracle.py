@@ -65,6 +65,12 @@ def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
 # ----------------------------------------------------------------------------
 # 1. gating
 # ----------------------------------------------------------------------------
+def router_logits(x: np.ndarray, router_w: np.ndarray) -> np.ndarray:
+    """The gate's linear layer before the top-k (the HF gate the axolotl
+    benchmark calls on the hidden states): logits[t, e] = x[t] . W[e], float64."""
+    return np.asarray(x, np.float64) @ np.asarray(router_w, np.float64).T
+
+
 def select_topk(logits: np.ndarray, k: int, allowed: Optional[np.ndarray] = None) -> np.ndarray:
     """Top-k expert ids per token, as k rounds of arg-max.
 

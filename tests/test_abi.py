@@ -225,3 +225,22 @@ def test_fused_forward_mxfp8_validation(L):
         args = [fake] * 17
         args[i] = None
         assert L.moe_fused_forward_mxfp8(ctypes.byref(ps), *args, ctypes.byref(ns), None) == -1
+
+
+def test_fused_forward_router_validation(L):
+    """Router entry point: the workspace is the layer's; router_w is required
+    and 16-byte aligned; router_logits_out may be NULL."""
+    p = _layer(H=64, I=64).c_struct()
+    n = ctypes.c_size_t(0)
+    assert L.moe_fused_forward_router(ctypes.byref(p), *([None] * 14), ctypes.byref(n), None) == 0
+    nb = ctypes.c_size_t(0)
+    assert L.moe_fused_forward(ctypes.byref(p), *([None] * 13), ctypes.byref(nb), None) == 0
+    assert n.value == nb.value > 0
+    fake = 1 << 20
+    ok = ctypes.c_size_t(n.value)
+    args = [fake] * 14
+    args[1] = None   # router_w missing
+    assert L.moe_fused_forward_router(ctypes.byref(p), *args, ctypes.byref(ok), None) == -1
+    args = [fake] * 14
+    args[1] = fake + 4   # router_w misaligned
+    assert L.moe_fused_forward_router(ctypes.byref(p), *args, ctypes.byref(ok), None) == -5

@@ -568,3 +568,14 @@ def test_mxfp8_layer_equals_layer_on_decoded_weights():
         dec[name] = bits
     want = O.moe_forward_cfg(cfg, dec)["out"]
     np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------- router logits
+def test_router_logits_bruteforce():
+    rng = np.random.default_rng(30)
+    x, wr = rng.standard_normal((3, 5)), rng.standard_normal((4, 5))
+    got = O.router_logits(x, wr)
+    for t in range(3):
+        for e in range(4):
+            s = sum(float(x[t, h]) * float(wr[e, h]) for h in range(5))
+            assert abs(got[t, e] - s) <= 1e-12 * max(1.0, abs(s))
