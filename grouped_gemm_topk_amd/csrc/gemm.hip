@@ -22,8 +22,10 @@
 // between the MFMAs of the current one instead of being issued as a burst,
 // which kept the address queue full and stalled the issuing waves.  The LDS
 // chunk order is XOR-swizzled so the MFMA operand reads are free of bank
-// conflicts.  Workgroups are mapped to tiles XCD by XCD (each XCD gets a
-// contiguous tile range) and, inside a range, the tiles of one expert's run
+// conflicts.  Workgroups are mapped to tiles XCD by XCD (each XCD gets an
+// equal, contiguous range of the tiles whose m-blocks hold rows; the grid is
+// sized for the align capacity and the rest exit) and, inside a range, the
+// tiles of one expert's run
 // of M-blocks are consecutive, in chunks of 8 M-blocks per N-tile, so that a
 // weight tile and the token rows are reused from that XCD's L2 (the L2
 // grouping / cache-aware scheduling of the skill card's *Optimization
@@ -187,9 +189,15 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) grouped_gemm_ker
     a_bytes = ((int64_t)p.a_rows * p.lda - beg) * 2;
     w_bytes = ((int64_t)p.N * p.ldw - beg) * 2;
   } else {
-    const int tg = xcd_tile(blockIdx.x, ntn * (pin.mblocks + pin.nsb));
+    // only the tiles of m-blocks that hold rows are mapped (the grid is sized
+    // for the align capacity): workgroups past them exit, and since the
+    // workgroups go to the XCDs round-robin, every XCD gets an equal share
+    const int vbr = min(pin.mblocks, ((pin.ntpp ? *pin.ntpp : pin.M) + BM - 1) / BM);
+    const int nvalid = ntn * (vbr + pin.nsb);
+    if ((int)blockIdx.x >= nvalid) return;
+    const int tg = xcd_tile(blockIdx.x, nvalid);
     // tiles past the routed ones belong to the dense second part
-    const bool second = tg >= ntn * pin.mblocks;
+    const bool second = tg >= ntn * vbr;
     if (second) {
       p.A = pin.A2;
       p.W = pin.W2;
@@ -204,8 +212,8 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) grouped_gemm_ker
       p.c_row_offset = pin.c2_row_offset;
       p.topk_w = nullptr;
     }
-    const int nmb = second ? pin.nsb : pin.mblocks;
-    const int t = second ? tg - ntn * pin.mblocks : tg;
+    const int nmb = second ? pin.nsb : vbr;
+    const int t = second ? tg - ntn * vbr : tg;
     const int total_rows = p.ntpp ? *p.ntpp : p.M;
     const int vb = min(nmb, (total_rows + BM - 1) / BM);   // m-blocks holding rows
     const int mb0 = t / ntn;
