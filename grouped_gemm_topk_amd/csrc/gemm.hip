@@ -22,14 +22,17 @@
 // between the MFMAs of the current one instead of being issued as a burst,
 // which kept the address queue full and stalled the issuing waves.  The LDS
 // chunk order is XOR-swizzled so the MFMA operand reads are free of bank
-// conflicts.  Workgroups are mapped to tiles XCD by XCD (each XCD gets an
-// equal, contiguous range of the tiles whose m-blocks hold rows; the grid is
-// sized for the align capacity and the rest exit) and, inside a range, the
-// tiles of one expert's run
-// of M-blocks are consecutive, in chunks of 8 M-blocks per N-tile, so that a
-// weight tile and the token rows are reused from that XCD's L2 (the L2
-// grouping / cache-aware scheduling of the skill card's *Optimization
-// Patterns*).
+// conflicts.  Tiles are numbered XCD by XCD (each XCD gets an equal,
+// contiguous range of the tiles whose m-blocks hold rows) and, inside a
+// range, the tiles of one expert's run of M-blocks are consecutive, in chunks
+// of 8 M-blocks per N-tile, so that a weight tile and the token rows are
+// reused from that XCD's L2 (the L2 grouping / cache-aware scheduling of the
+// skill card's *Optimization Patterns*).  With the 128-row tile the grid is
+// one workgroup per CU and each workgroup runs a sequence of tiles: between
+// two tiles it requests the next tile's first K steps and then writes the
+// finished tile while they are in flight, and the global reads a tile's
+// set-up needs (sorted token ids, routed weights) are issued a tile ahead;
+// the expert ids of the m-blocks sit in LDS for the tile mapping.
 // v_mfma_f32_32x32x16_bf16 is used when a wave owns >= 32 token rows,
 // v_mfma_f32_16x16x32_bf16 for BLOCK_M = 16.
 #include <hip/hip_runtime.h>
@@ -46,17 +49,13 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 
 
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  unsigned u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;  // NaN
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
-
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+// silu(z) = z * sigmoid(z) with the hardware reciprocal (the result is rounded
+// to bf16 next)
+__device__ __forceinline__ float silu(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 template <int MT>
 struct Mfma;
@@ -113,23 +112,34 @@ __device__ __forceinline__ int xcd_tile(int L, int n) {
 }
 
 // [rs, re): the maximal run of m-blocks around mb0 (below vb) that hold the
-// same expert id; wave-uniform, 64 ids per probe.
-__device__ __forceinline__ void expert_run(const int* __restrict__ expert_ids, int mb0, int vb,
-                                           int lane, int& rs, int& re) {
-  const int e0 = expert_ids[mb0];
-  for (int base = mb0 - 1;; base -= 64) {
-    const int idx = base - lane;
-    const bool stop = idx < 0 || expert_ids[idx < 0 ? 0 : idx] != e0;
-    const uint64_t b = __ballot(stop);
-    if (b) { rs = base - (int)__builtin_ctzll(b) + 1; break; }
+// expert e0 = id(mb0); wave-uniform, 64 ids per probe (both directions'
+// first probes read together); id(i) gives the expert id of m-block i.
+template <typename Id>
+__device__ __forceinline__ void expert_run(Id id, int mb0, int vb, int lane, int e0, int& rs,
+                                           int& re) {
+  auto probe_lo = [&](int base, int v) { const int i = base - lane; return i < 0 || v != e0; };
+  auto probe_hi = [&](int base, int v) { const int i = base + lane; return i >= vb || v != e0; };
+  auto at = [&](int i) { return id(i < 0 ? 0 : (i >= vb ? mb0 : i)); };
+  int lo = mb0 - 1, hi = mb0 + 1;
+  const int vlo = at(lo - lane), vhi = at(hi + lane);
+  uint64_t b = __ballot(probe_lo(lo, vlo));
+  while (!b) {
+    lo -= 64;
+    b = __ballot(probe_lo(lo, at(lo - lane)));
   }
-  for (int base = mb0 + 1;; base += 64) {
-    const int idx = base + lane;
-    const bool stop = idx >= vb || expert_ids[idx >= vb ? mb0 : idx] != e0;
-    const uint64_t b = __ballot(stop);
-    if (b) { re = base + (int)__builtin_ctzll(b); break; }
+  rs = lo - (int)__builtin_ctzll(b) + 1;
+  b = __ballot(probe_hi(hi, vhi));
+  while (!b) {
+    hi += 64;
+    b = __ballot(probe_hi(hi, at(hi + lane)));
   }
+  re = hi + (int)__builtin_ctzll(b);
 }
+
+// expert ids kept in LDS by the 128-row tile (its three stages leave 16 KB of
+// the 160 KB; the smaller tiles run two workgroups per CU and keep none)
+template <int BM>
+constexpr int kEidsLds = BM == 128 ? 2048 : 0;
 
 // BM token rows x BNW weight rows per workgroup tile, WAVES_M x WAVES_N waves,
 // BK-wide K steps, NS LDS stages (direct path: loads for step kt + NS - 1 are
@@ -166,86 +176,173 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) grouped_gemm_ker
   const int wn = wave % WAVES_N;
   const int wm = wave / WAVES_N;
 
-  // ---- tile of this workgroup: XCD-contiguous; the tiles of each expert's
-  // run of m-blocks are consecutive, in chunks of GM m-blocks with the n-tile
-  // outer, so that neighbouring workgroups share weight tiles and token rows
+  // ---- the tiles of this launch.  Tiles are numbered XCD by XCD: tile L of
+  // the launch's sequence goes to XCD L mod 8 (the order in which workgroups
+  // are handed to the XCDs), and each XCD owns an equal, contiguous range of
+  // tile indices.  Inside a range the tiles of each expert's run of m-blocks
+  // are consecutive, in chunks of GM m-blocks with the n-tile outer, so that
+  // the workgroups running at the same time on one XCD share weight tiles and
+  // token rows in its L2.  Only the tiles of m-blocks that hold rows are
+  // numbered (the grid is sized for the align capacity).  A workgroup runs
+  // tiles blockIdx.x, blockIdx.x + gridDim.x, ... (the grid is one workgroup
+  // per CU when it has more tiles than that).  Between two tiles it requests
+  // the next tile's first K steps and writes the finished tile while they are
+  // in flight; the global reads a tile's set-up needs (sorted token ids,
+  // routed weights) are issued one tile ahead, so they land with those loads.
   const int ntn = pin.ntiles_n;
-  GemmParams p = pin;
-  int mb, nt;
-  const uint16_t* We;
-  int64_t a_bytes, w_bytes;   // bytes the A / W descriptors may reach
+  int vbr = 0, nvalid;
   if (pin.nseg > 0) {
-    // segmented reduction: segment s is a dense product over its own columns
-    const int per = ntn * pin.mblocks;
-    const int tg = xcd_tile(blockIdx.x, per * pin.nseg);
-    const int sg = tg / per, r = tg - sg * per;
-    mb = r % pin.mblocks;
-    nt = r / pin.mblocks;
-    const int beg = pin.seg_beg[sg];
-    p.K = pin.seg_end[sg] - beg;
-    p.A = pin.A + beg;
-    We = pin.W + beg;
-    p.C = (char*)pin.C + sg * pin.seg_c_stride * (pin.c_fp32 ? 4 : 2);
-    a_bytes = ((int64_t)p.a_rows * p.lda - beg) * 2;
-    w_bytes = ((int64_t)p.N * p.ldw - beg) * 2;
+    nvalid = ntn * pin.mblocks * pin.nseg;
   } else {
-    // only the tiles of m-blocks that hold rows are mapped (the grid is sized
-    // for the align capacity): workgroups past them exit, and since the
-    // workgroups go to the XCDs round-robin, every XCD gets an equal share
-    const int vbr = min(pin.mblocks, ((pin.ntpp ? *pin.ntpp : pin.M) + BM - 1) / BM);
-    const int nvalid = ntn * (vbr + pin.nsb);
-    if ((int)blockIdx.x >= nvalid) return;
-    const int tg = xcd_tile(blockIdx.x, nvalid);
-    // tiles past the routed ones belong to the dense second part
-    const bool second = tg >= ntn * vbr;
-    if (second) {
-      p.A = pin.A2;
-      p.W = pin.W2;
-      p.E = 1;
-      p.a_row_div = 0;
-      p.sorted_ids = nullptr;
-      p.expert_ids = nullptr;
-      p.ntpp = nullptr;
-      p.M = pin.M2;
-      p.a_rows = pin.M2;
-      p.C = pin.C2;
-      p.c_row_offset = pin.c2_row_offset;
-      p.topk_w = nullptr;
-    }
-    const int nmb = second ? pin.nsb : vbr;
-    const int t = second ? tg - ntn * vbr : tg;
-    const int total_rows = p.ntpp ? *p.ntpp : p.M;
-    const int vb = min(nmb, (total_rows + BM - 1) / BM);   // m-blocks holding rows
-    const int mb0 = t / ntn;
-    if (mb0 >= vb) return;
-    int rs = 0, re = vb;
-    if (p.expert_ids) expert_run(p.expert_ids, mb0, vb, lane, rs, re);
-    constexpr int GM = MOE_GM;
-    const int jr = t - rs * ntn;
-    const int grp = jr / (GM * ntn);
-    const int gsz = min(GM, re - rs - grp * GM);
-    const int j = jr - grp * GM * ntn;
-    mb = rs + grp * GM + j % gsz;
-    nt = j / gsz;
-    const int e = p.expert_ids ? p.expert_ids[mb] : 0;
-    if (e < 0 || e >= p.E) return;
-    We = p.W + (int64_t)e * p.N * p.ldw;
-    a_bytes = (int64_t)p.a_rows * p.lda * 2;
-    w_bytes = (int64_t)p.N * p.ldw * 2;
+    vbr = min(pin.mblocks, ((pin.ntpp ? *pin.ntpp : pin.M) + BM - 1) / BM);
+    nvalid = ntn * (vbr + pin.nsb);
   }
-  const int m0 = mb * BM;
-  const int ncols = SW ? p.I : p.N;           // output columns
-  const int n0 = nt * (SW ? BNW / 2 : BNW);
-
+  if ((int)blockIdx.x >= nvalid) return;
+  const int G = gridDim.x;
+  const int ncols = SW ? pin.I : pin.N;   // output columns
+  constexpr int GM = MOE_GM;
   // kNoRow: an offset beyond every descriptor even after the K advance is
   // added, so the load reads zeros
   constexpr int kNoRow = 0x7fff0000;
 
-  // ---- direct-to-LDS: lane l of a wave load fills LDS unit (base + l); the
-  // unit at (row r, position pos) holds global chunk pos ^ mask(r), so the
-  // source offsets carry the swizzle and each row's lanes still read one line
-  int xdo[XL], wdo[WL];
-  {
+  // the expert ids of the routed m-blocks, copied to LDS once per workgroup
+  // (every tile's mapping reads them) when the tile's LDS leaves room
+  typedef __attribute__((address_space(3))) int lds_int;
+  lds_int* s_eids = nullptr;
+  if constexpr (kEidsLds<BM> > 0) {
+    __shared__ int s_eids_buf[kEidsLds<BM> > 0 ? kEidsLds<BM> : 1];
+    s_eids = (lds_int*)s_eids_buf;
+  }
+  const bool eids_lds = kEidsLds<BM> > 0 && pin.nseg == 0 && pin.expert_ids && vbr <= kEidsLds<BM>;
+  if (eids_lds) {
+    for (int i = tid; i < vbr; i += NT) s_eids[i] = pin.expert_ids[i];
+    __syncthreads();
+  }
+  auto eid = [&](int i) -> int {
+    if (eids_lds) return s_eids[i];
+    return pin.expert_ids[i];
+  };
+
+  // a tile's place: m-block, n-tile, expert (the segment in segmented launches)
+  struct Map {
+    int mb, nt, e;
+    bool second, store;   // dense second part; false only for an invalid expert id
+  };
+  auto resolve = [&](int Lt) -> Map {
+    Map m;
+    m.store = true;
+    m.second = false;
+    const int tg = xcd_tile(Lt, nvalid);
+    if (pin.nseg > 0) {
+      // segmented reduction: segment s is a dense product over its own columns
+      const int per = ntn * pin.mblocks;
+      const int sg = tg / per, r = tg - sg * per;
+      m.mb = r % pin.mblocks;
+      m.nt = r / pin.mblocks;
+      m.e = sg;
+      return m;
+    }
+    // tiles past the routed ones belong to the dense second part
+    m.second = tg >= ntn * vbr;
+    const int vb = m.second ? pin.nsb : vbr;
+    const int tl = m.second ? tg - ntn * vbr : tg;
+    const int mb0 = tl / ntn;   // < vb for every numbered tile
+    int rs = 0, re = vb, e = 0;
+    if (!m.second && pin.expert_ids) {
+      e = eid(mb0);   // the expert of the whole run
+      expert_run(eid, mb0, vb, lane, e, rs, re);
+    }
+    const int jr = tl - rs * ntn;
+    const int grp = jr / (GM * ntn);
+    const int gsz = min(GM, re - rs - grp * GM);
+    const int j = jr - grp * GM * ntn;
+    m.mb = rs + grp * GM + j % gsz;
+    m.nt = j / gsz;
+    if (!m.second && (e < 0 || e >= pin.E)) {   // computed, not written
+      m.store = false;
+      e = 0;
+    }
+    m.e = e;
+    return m;
+  };
+
+  // what a tile's loads and stores use
+  struct Tile {
+    const uint16_t* A;        // token rows (at the segment's first column)
+    const uint16_t* W;        // this tile's expert weights
+    char* C;                  // output base
+    const int* sorted;        // sorted token ids (nullptr: rows in order)
+    const float* topk_w;      // routed weights of the scatter epilogue
+    int64_t c_row_offset, a_bytes, w_bytes;
+    int a_row_div, M, K, m0, n0;
+    bool store;
+  };
+  auto tile_of = [&](const Map& m) -> Tile {
+    Tile t;
+    t.store = m.store;
+    t.m0 = m.mb * BM;
+    t.n0 = m.nt * (SW ? BNW / 2 : BNW);
+    t.K = pin.K;
+    if (pin.nseg > 0) {
+      const int beg = pin.seg_beg[m.e];
+      t.K = pin.seg_end[m.e] - beg;
+      t.A = pin.A + beg;
+      t.W = pin.W + beg;
+      t.C = (char*)pin.C + m.e * pin.seg_c_stride * (pin.c_fp32 ? 4 : 2);
+      t.sorted = pin.sorted_ids;
+      t.topk_w = pin.topk_w;
+      t.c_row_offset = pin.c_row_offset;
+      t.a_row_div = pin.a_row_div;
+      t.M = pin.M;
+      t.a_bytes = ((int64_t)pin.a_rows * pin.lda - beg) * 2;
+      t.w_bytes = ((int64_t)pin.N * pin.ldw - beg) * 2;
+    } else if (m.second) {
+      t.A = pin.A2;
+      t.W = pin.W2;
+      t.C = (char*)pin.C2;
+      t.sorted = nullptr;
+      t.topk_w = nullptr;
+      t.c_row_offset = pin.c2_row_offset;
+      t.a_row_div = 0;
+      t.M = pin.M2;
+      t.a_bytes = (int64_t)pin.M2 * pin.lda * 2;
+      t.w_bytes = (int64_t)pin.N * pin.ldw * 2;
+    } else {
+      t.A = pin.A;
+      t.W = pin.W + (int64_t)m.e * pin.N * pin.ldw;
+      t.C = (char*)pin.C;
+      t.sorted = pin.sorted_ids;
+      t.topk_w = pin.topk_w;
+      t.c_row_offset = pin.c_row_offset;
+      t.a_row_div = pin.a_row_div;
+      t.M = pin.M;
+      t.a_bytes = (int64_t)pin.a_rows * pin.lda * 2;
+      t.w_bytes = (int64_t)pin.N * pin.ldw * 2;
+    }
+    return t;
+  };
+
+  // sorted ids of the token rows this thread loads (XL) and of the rows its
+  // lane writes (FM): global reads, issued a tile ahead
+  auto load_ids = [&](const Tile& t, int* xs, int* es) {
+#pragma unroll
+    for (int q = 0; q < XL; ++q) {
+      const int u = tid + NT * q;
+      const int i = t.m0 + u / CPR;
+      xs[q] = (u < BM * CPR && t.sorted) ? t.sorted[i] : i;
+    }
+#pragma unroll
+    for (int q = 0; q < FM; ++q) {
+      const int i = t.m0 + wm * WM + q * MT + M::out_col(lane);
+      es[q] = t.sorted ? t.sorted[i] : i;
+    }
+  };
+
+  // direct-to-LDS source offsets: lane l of a wave load fills LDS unit
+  // (base + l); the unit at (row r, position pos) holds global chunk
+  // pos ^ mask(r), so the offsets carry the swizzle and each row's lanes still
+  // read one line
+  auto offsets = [&](const Tile& t, const int* xs, int* xdo, int* wdo) {
 #pragma unroll
     for (int q = 0; q < XL; ++q) {
       const int u = tid + NT * q;
@@ -253,15 +350,15 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) grouped_gemm_ker
       const int c = (u % CPR) ^ ((r / (16 / CPR)) % CPR);
       xdo[q] = kNoRow;
       if (u < BM * CPR) {
-        const int i = m0 + r;
+        const int i = t.m0 + r;
         int arow = -1;
-        if (p.sorted_ids) {
-          const int sid = p.sorted_ids[i];
-          if (sid >= 0 && sid < p.num_valid) arow = p.a_row_div ? sid / p.a_row_div : i;
-        } else if (i < p.M) {
+        if (t.sorted) {
+          const int sid = xs[q];
+          if (sid >= 0 && sid < pin.num_valid) arow = t.a_row_div ? sid / t.a_row_div : i;
+        } else if (i < t.M) {
           arow = i;
         }
-        if (arow >= 0) xdo[q] = arow * p.lda * 2 + c * 16;
+        if (arow >= 0) xdo[q] = arow * pin.lda * 2 + c * 16;
       }
     }
 #pragma unroll
@@ -272,16 +369,47 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) grouped_gemm_ker
       int g;
       bool ok;
       if (SW) {
-        const int cc = r < BNW / 2 ? n0 + r : n0 + r - BNW / 2;
-        ok = cc < p.I;
-        g = r < BNW / 2 ? cc : p.I + cc;
+        const int cc = r < BNW / 2 ? t.n0 + r : t.n0 + r - BNW / 2;
+        ok = cc < pin.I;
+        g = r < BNW / 2 ? cc : pin.I + cc;
       } else {
-        g = n0 + r;
-        ok = g < p.N;
+        g = t.n0 + r;
+        ok = g < pin.N;
       }
-      wdo[q] = ok ? g * p.ldw * 2 + c * 16 : kNoRow;
+      wdo[q] = ok ? g * pin.ldw * 2 + c * 16 : kNoRow;
     }
-  }
+  };
+
+  // epilogue rows of this lane (the q-th MFMA column block): output row,
+  // whether it is written, and its routed weight (read a tile ahead)
+  const int epi = pin.epi;
+  struct EpiRows {
+    int64_t orow[FM];
+    int sid[FM];
+    bool ok[FM];
+  };
+  auto epi_rows = [&](const Tile& t, const int* es, EpiRows& er) {
+#pragma unroll
+    for (int q = 0; q < FM; ++q) {
+      const int i = t.m0 + wm * WM + q * MT + M::out_col(lane);
+      if (epi == 3) {
+        const int sid = es[q];
+        const bool ok = t.sorted ? (sid >= 0 && sid < pin.num_valid) : i < t.M;
+        er.sid[q] = sid;
+        er.orow[q] = t.c_row_offset + sid;
+        er.ok[q] = ok && t.store;
+      } else {
+        er.sid[q] = i;
+        er.ok[q] = (t.sorted ? true : i < t.M) && t.store;
+        er.orow[q] = i;
+      }
+    }
+  };
+  auto load_scale = [&](const Tile& t, const EpiRows& er, float* sc) {
+#pragma unroll
+    for (int q = 0; q < FM; ++q)
+      sc[q] = (epi == 3 && t.topk_w && er.ok[q]) ? t.topk_w[er.sid[q]] : 1.f;
+  };
 
   // ---- LDS read addresses: every operand row a lane reads is row(lane) plus
   // a multiple of 16, which keeps the swizzle mask of row(lane); so per
@@ -302,28 +430,29 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) grouped_gemm_ker
   };
 
   typename M::acc_t acc[FN][FM];
-#pragma unroll
-  for (int f = 0; f < FN; ++f)
-#pragma unroll
-    for (int q = 0; q < FM; ++q)
-#pragma unroll
-      for (int v = 0; v < M::kVals; ++v) acc[f][q][v] = 0.f;
 
   // direct-to-LDS loads of K step kt into LDS buffer b.  Issued from inline
   // asm (buffer_load_dwordx4 ... lds; M0 holds the wave's LDS destination and
   // is restored) so that the compiler, which cannot tell the in-flight
   // transfers from the LDS reads of other buffers, does not wait for all of
   // them before every read; completion is awaited explicitly (vmcnt) before
-  // the barrier that publishes a step.  The asm writes no register.
+  // the barrier that publishes a step.  The asm writes no register.  Ordinary
+  // loads (tile setup, epilogue rows) are waited for explicitly before the
+  // next direct loads are issued, so that no wait the compiler places for
+  // them falls inside the pipeline.
   typedef int i32x4 __attribute__((ext_vector_type(4)));
+  // (the words are made wave-uniform explicitly: the asm takes them in SGPRs)
   auto rsrc4 = [](const void* base, int64_t bytes) {
     const uint64_t a = (uint64_t)base;
-    return i32x4{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xffffu), (int)bytes, 0x00020000};
+    return i32x4{__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+                 __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu)),
+                 __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000};
   };
-  const i32x4 xr4 = rsrc4(p.A, a_bytes);
-  const i32x4 wr4 = rsrc4(We, w_bytes);
-  auto dma1 = [](const i32x4& rs, const void* lds, int voff, int soff) {
-    const unsigned la = (unsigned)(uintptr_t)(const __attribute__((address_space(3))) void*)lds;
+  // la: LDS byte address of the wave's 64 destination units (wave-uniform:
+  // each wave fills its own block of units)
+  auto dma1 = [](const i32x4& rs, unsigned la, int voff, int soff) {
+    const unsigned l = la;
+    const int so = soff;
     int m0save;
     asm volatile(
         "s_mov_b32 %0, m0\n\t"
@@ -331,9 +460,31 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) grouped_gemm_ker
         "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
         "s_mov_b32 m0, %0"
         : "=&s"(m0save)
-        : "s"(la), "v"(voff), "s"(rs), "s"(soff)
+        : "s"(l), "v"(voff), "s"(rs), "s"(so)
         : "memory");
   };
+  typedef const __attribute__((address_space(3))) void* lds_cptr;
+  const unsigned lds_x = (unsigned)(uintptr_t)(lds_cptr)&sX[0][0];
+  const unsigned lds_w = (unsigned)(uintptr_t)(lds_cptr)&sW[0][0];
+  // vmcnt(n) with the other counters left alone
+#define MOE_VMW(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+
+  // the first tile, set up in full
+  int L = blockIdx.x;
+  Tile cur = tile_of(resolve(L));
+  int xs[XL], es[FM];
+  load_ids(cur, xs, es);
+  MOE_VMW(0);
+  int xdo[XL], wdo[WL];
+  EpiRows er;
+  float sc[FM];
+  offsets(cur, xs, xdo, wdo);
+  epi_rows(cur, es, er);
+  load_scale(cur, er, sc);
+  i32x4 xr4 = rsrc4(cur.A, cur.a_bytes);
+  i32x4 wr4 = rsrc4(cur.W, cur.w_bytes);
+  int K = cur.K;
+
   // this wave issues the last of the XL token-row loads (waves past the end of
   // the token tile skip it)
   const bool x_wave = NT * (XL - 1) + 64 * wave < BM * CPR;
@@ -350,20 +501,22 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) grouped_gemm_ker
     int off = is_x ? xdo[is_x ? q : 0] : wdo[is_x ? 0 : q], soff = k0 * 2;
     if constexpr (tail) {
       const int c = (u % CPR) ^ ((u / CPR / (16 / CPR)) % CPR);
-      off = (k0 + c * 8 < p.K && off != kNoRow) ? off + k0 * 2 : kNoRow;
+      off = (k0 + c * 8 < K && off != kNoRow) ? off + k0 * 2 : kNoRow;
       soff = 0;
     }
-    if (is_x) dma1(xr4, sX[b] + NT * q + 64 * wave, off, soff);
-    else dma1(wr4, sW[b] + NT * q + 64 * wave, off, soff);
+    if (is_x) dma1(xr4, lds_x + (unsigned)((b * BM * CPR + NT * q + 64 * wave) * 16), off, soff);
+    else dma1(wr4, lds_w + (unsigned)((b * BNW * CPR + NT * q + 64 * wave) * 16), off, soff);
   };
-  // one whole K step of direct loads into LDS buffer b
-  auto dma_step = [&](auto tail_c, int kt, int b) {
+  // the direct loads [i0, i1) of K step kt into LDS buffer b (all of them:
+  // [0, XL + WL); the weight chunks alone: [XL, XL + WL))
+  auto dma_part = [&](int kt, int b, int i0, int i1) {
+    const bool tail = (kt + 1) * BK > K;
 #pragma unroll
-    for (int i = 0; i < XL + WL; ++i) dma_one(tail_c, kt, b, i);
-  };
-  auto dma = [&](int kt, int b) {
-    if ((kt + 1) * BK > p.K) dma_step(std::true_type{}, kt, b);
-    else dma_step(std::false_type{}, kt, b);
+    for (int i = 0; i < XL + WL; ++i) {
+      if (i < i0 || i >= i1) continue;
+      if (tail) dma_one(std::true_type{}, kt, b, i);
+      else dma_one(std::false_type{}, kt, b, i);
+    }
   };
   // operand registers of one k-substep
   struct Ops {
@@ -394,38 +547,56 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) grouped_gemm_ker
   };
 
   // ---- pipeline over K steps, one barrier per step.
-  // NBUF = NS buffers, D = NS - 1: step kt computes from buffer
-  // kt % NBUF while its MFMAs interleave the loads of step kt + D into the
-  // buffer that step kt - 1 used (every wave is past the barrier that ended
-  // step kt - 1); then each thread waits for its own loads of step kt + 1 and
-  // the barrier makes them visible to all waves.
-  const int nk = (p.K + BK - 1) / BK;
-  {
-    // vmcnt(n) with the other counters left alone; n = loads one thread
-    // issues per K step (a compile-time count per kind of wave)
-    constexpr int NXW = XL + WL;
-    constexpr int NW = WL + XL - 1;
-    static_assert((BM * CPR - NT * (XL - 1)) % 64 == 0, "the last token-row load is whole waves");
-    constexpr int D = NBUF - 1;   // prefetch distance in K steps
-    static_assert((D - 1) * NXW <= 63, "vmcnt range");
-    // wait until this thread's loads of the oldest pending step have landed;
-    // in steady state D - 1 later steps stay in flight (a compile-time count
-    // per kind of wave), near the end of K everything is waited for
-#define MOE_VMW(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
-    auto wait_steady = [&]() {
-      if (x_wave) MOE_VMW((D - 1) * NXW); else MOE_VMW((D - 1) * NW);
-    };
-    auto wait_all = [&]() { MOE_VMW(0); };
-#undef MOE_VMW
+  // NBUF = NS buffers, D = NS - 1: step kt computes from buffer b0 while its
+  // MFMAs interleave the loads of step kt + D into the buffer that step
+  // kt - 1 used (every wave is past the barrier that ended step kt - 1); then
+  // each thread waits for its own loads of step kt + 1 and the barrier makes
+  // them visible to all waves.  The ring continues from tile to tile: the next
+  // tile's first D steps go to the D buffers the last step did not read.
+  constexpr int NXW = XL + WL;
+  constexpr int NW = WL + XL - 1;
+  static_assert((BM * CPR - NT * (XL - 1)) % 64 == 0, "the last token-row load is whole waves");
+  constexpr int D = NBUF - 1;   // prefetch distance in K steps
+  static_assert((D - 1) * NXW <= 63, "vmcnt range");
+  // wait until this thread's loads of the oldest pending step have landed;
+  // in steady state D - 1 later steps stay in flight (a compile-time count
+  // per kind of wave), near the end of K everything is waited for
+  auto wait_steady = [&]() {
+    if (x_wave) MOE_VMW((D - 1) * NXW); else MOE_VMW((D - 1) * NW);
+  };
+  auto wait_all = [&]() { MOE_VMW(0); };
+  // the first D steps of the current tile into buffers b, b + 1, ...: the
+  // weight chunks first (they need no token index)
+  auto first_steps = [&](int b, int nk) {
     for (int st = 0; st < D; ++st)
-      if (st < nk) dma(st, st);
-    if (nk > D - 1) wait_steady(); else wait_all();
-    __builtin_amdgcn_s_barrier();
-    int b0 = 0;
+      if (st < nk) dma_part(st, (b + st) % NBUF, XL, XL + WL);
+    for (int st = 0; st < D; ++st)
+      if (st < nk) dma_part(st, (b + st) % NBUF, 0, XL);
+  };
+
+  int b0 = 0;
+  first_steps(0, (K + BK - 1) / BK);
+  // the second tile: mapping and row ids
+  int Ln = L + G;
+  Tile nxt = cur;
+  if (Ln < nvalid) {
+    nxt = tile_of(resolve(Ln));
+    load_ids(nxt, xs, es);
+  }
+  wait_all();
+  __builtin_amdgcn_s_barrier();
+  for (;;) {
+    const int nk = (K + BK - 1) / BK;
+#pragma unroll
+    for (int f = 0; f < FN; ++f)
+#pragma unroll
+      for (int q = 0; q < FM; ++q)
+#pragma unroll
+        for (int v = 0; v < M::kVals; ++v) acc[f][q][v] = 0.f;
     for (int kt = 0; kt < nk; ++kt) {
-      const int bd = b0 == 0 ? NBUF - 1 : b0 - 1;   // (kt + D) % NBUF
+      const int bd = b0 == 0 ? NBUF - 1 : b0 - 1;   // the buffer of step kt + D
       // 0: no load this step, 1: a full K step, 2: the ragged last K step
-      const int dmode = kt + D < nk ? ((kt + D + 1) * BK > p.K ? 2 : 1) : 0;
+      const int dmode = kt + D < nk ? ((kt + D + 1) * BK > K ? 2 : 1) : 0;
       auto load_i = [&](int i) {
         if (dmode == 1) dma_one(std::false_type{}, kt + D, bd, i);
         else if (dmode == 2) dma_one(std::true_type{}, kt + D, bd, i);
@@ -449,67 +620,96 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) grouped_gemm_ker
       }
       b0 = b0 == NBUF - 1 ? 0 : b0 + 1;
     }
-  }
 
-  // ---- epilogue
-  const int epi = p.epi;
+    // ---- between tiles (the same K: segmented launches run one tile per
+    // workgroup).  No direct load is in flight here, so waiting for the reads
+    // issued a tile ago costs nothing.
+    MOE_VMW(0);
+    const Tile done = cur;
+    const EpiRows der = er;
+    float dsc[FM];
 #pragma unroll
-  for (int q = 0; q < FM; ++q) {
-    const int mloc = wm * WM + q * MT + M::out_col(lane);
-    const int i = m0 + mloc;
-    int64_t orow;
-    float scale = 1.f;
-    bool ok;
-    if (epi == 3) {
-      int sid;
-      if (p.sorted_ids) {
-        sid = p.sorted_ids[i];
-        ok = sid >= 0 && sid < p.num_valid;
-      } else {
-        sid = i;
-        ok = i < p.M;
+    for (int q = 0; q < FM; ++q) dsc[q] = sc[q];
+    const bool more = Ln < nvalid;
+    if (more) {
+      // the next tile: its first D steps, then its routed weights
+      cur = nxt;
+      offsets(cur, xs, xdo, wdo);
+      epi_rows(cur, es, er);
+      xr4 = rsrc4(cur.A, cur.a_bytes);
+      wr4 = rsrc4(cur.W, cur.w_bytes);
+      K = cur.K;
+      first_steps(b0, (K + BK - 1) / BK);
+      load_scale(cur, er, sc);
+      // the tile after it: mapping and row ids
+      Ln += G;
+      if (Ln < nvalid) {
+        nxt = tile_of(resolve(Ln));
+        load_ids(nxt, xs, es);
       }
-      if (ok && p.topk_w) scale = p.topk_w[sid];
-      orow = p.c_row_offset + sid;
-    } else {
-      ok = p.sorted_ids ? true : i < p.M;
-      orow = i;
     }
-    if (!ok) continue;
-    constexpr int FO = SW ? FN / 2 : FN;
+
+    // ---- epilogue of the finished tile
 #pragma unroll
-    for (int f = 0; f < FO; ++f) {
-      const int colbase = SW ? n0 + wn * (BNW / 2 / WAVES_N) + f * MT : n0 + wn * WNW + f * MT;
+    for (int q = 0; q < FM; ++q) {
+      if (!der.ok[q]) continue;
+      const int64_t orow = der.orow[q];
+      const float scale = dsc[q];
+      constexpr int FO = SW ? FN / 2 : FN;
 #pragma unroll
-      for (int g = 0; g < M::kGroups; ++g) {
-        const int col = colbase + M::out_row(g, lane);
-        if (col >= ncols) continue;
-        float o[4];
+      for (int f = 0; f < FO; ++f) {
+        const int colbase = SW ? done.n0 + wn * (BNW / 2 / WAVES_N) + f * MT : done.n0 + wn * WNW + f * MT;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const float h = acc[f][q][4 * g + v];
-          if (SW) {
-            const float u = acc[f + FN / 2][q][4 * g + v];
-            o[v] = silu(h) * u;
-          } else if (epi == 2) {
-            const float r = fmaxf(h, 0.f);
-            o[v] = r * r;
+        for (int g = 0; g < M::kGroups; ++g) {
+          const int col = colbase + M::out_row(g, lane);
+          if (col >= ncols) continue;
+          float o[4];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const float h = acc[f][q][4 * g + v];
+            if (SW) {
+              const float u = acc[f + FN / 2][q][4 * g + v];
+              o[v] = silu(h) * u;
+            } else if (epi == 2) {
+              const float r = fmaxf(h, 0.f);
+              o[v] = r * r;
+            } else {
+              o[v] = h * scale;
+            }
+          }
+          if (pin.c_fp32) {
+            float4* dst = (float4*)((float*)done.C + orow * pin.ldc + col);
+            *dst = make_float4(o[0], o[1], o[2], o[3]);
           } else {
-            o[v] = h * scale;
+            const bf16x2 lo = {(__bf16)o[0], (__bf16)o[1]}, hi = {(__bf16)o[2], (__bf16)o[3]};
+            uint2 pk;
+            pk.x = __builtin_bit_cast(unsigned, lo);
+            pk.y = __builtin_bit_cast(unsigned, hi);
+            *(uint2*)((uint16_t*)done.C + orow * pin.ldc + col) = pk;
           }
         }
-        if (p.c_fp32) {
-          float4* dst = (float4*)((float*)p.C + orow * p.ldc + col);
-          *dst = make_float4(o[0], o[1], o[2], o[3]);
-        } else {
-          uint2 pk;
-          pk.x = (unsigned)f32_to_bf16(o[0]) | ((unsigned)f32_to_bf16(o[1]) << 16);
-          pk.y = (unsigned)f32_to_bf16(o[2]) | ((unsigned)f32_to_bf16(o[3]) << 16);
-          *(uint2*)((uint16_t*)p.C + orow * p.ldc + col) = pk;
-        }
       }
     }
+    if (!more) break;
+    // the next tile's first steps (and this tile's stores) have landed
+    wait_all();
+    __builtin_amdgcn_s_barrier();
   }
+#undef MOE_VMW
+}
+
+// compute units of the current device (cached per device; 0 if unknown)
+int cu_count() {
+  constexpr int kMaxDev = 64;
+  static int cache[kMaxDev];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 0;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cache[dev] = n;
+  }
+  return cache[dev];
 }
 
 template <int BM, int BNW, int WAVES_M, int WAVES_N, int BK, int NS, int MINW>
@@ -521,8 +721,15 @@ hipError_t launch_bm(GemmParams p, hipStream_t s) {
   p.nsb = p.M2 > 0 ? (p.M2 + BM - 1) / BM : 0;
   p.ntiles_n = (ncols + tile_n - 1) / tile_n;
   if (p.nseg > 0) p.nsb = 0;
-  const int64_t nwg = (int64_t)(p.mblocks + p.nsb) * p.ntiles_n * (p.nseg > 0 ? p.nseg : 1);
+  int64_t nwg = (int64_t)(p.mblocks + p.nsb) * p.ntiles_n * (p.nseg > 0 ? p.nseg : 1);
   if (nwg == 0) return hipSuccess;
+  // one workgroup per CU (the LDS of the 128-row tile admits no second one),
+  // each running tiles gridDim.x apart; the CU count is a multiple of 8, so a
+  // workgroup stays on the XCD its tiles are numbered for
+  if (BM == 128 && p.nseg == 0) {
+    const int ncu = cu_count();
+    if (ncu > 0 && ncu % 8 == 0 && nwg > ncu) nwg = ncu;
+  }
   if (sw)
     hipLaunchKernelGGL((grouped_gemm_kernel<BM, BNW, WAVES_M, WAVES_N, true, BK, NS, MINW>),
                        dim3((unsigned)nwg), dim3(64 * WAVES_M * WAVES_N), 0, s, p);
