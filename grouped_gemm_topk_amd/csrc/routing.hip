@@ -38,9 +38,28 @@ __device__ __forceinline__ double wave_sum(double v) {
 
 __device__ __forceinline__ double sigmoid64(double l) { return 1.0 / (1.0 + exp(-l)); }
 
+// 64-bit key whose unsigned order is the selection order: high word = an
+// order-preserving image of the logit (-0 folded into +0, so the two compare
+// equal as floats do), low word = the inverted expert index (ties to the
+// lower index).  0 is below every key of an expert.
+__device__ __forceinline__ uint64_t order_key(float f, int e) {
+  unsigned u = __float_as_uint(f + 0.0f);
+  u ^= (unsigned)((int)u >> 31) | 0x80000000u;
+  return ((uint64_t)u << 32) | (uint64_t)(0xffffffffu - (unsigned)e);
+}
+
+// LDS writes of this wave visible to its other lanes
+__device__ __forceinline__ void wave_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Gating of token t by the calling wave.  `s_sig` is per-wave LDS scratch of
-// MOE_MAX_EXPERTS doubles, `s_keep` per-wave scratch of 64 ints (group flags).
-// Returns through lane j < k: *out_id, *out_w.
+// MOE_MAX_EXPERTS doubles, `s_keep` per-wave scratch of 64 ints.  Returns
+// through lane j < k: *out_id, *out_w.  Ranks and sums go through LDS (one
+// broadcast read per value) rather than chains of cross-lane shuffles; with
+// more than 128 experts the top-k is k rounds of a butterfly arg-max.
 __device__ void gate_token(const GateParams& p, int t, double* s_sig, int* s_keep,
                            int* out_id, float* out_w) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -61,88 +80,134 @@ __device__ void gate_token(const GateParams& p, int t, double* s_sig, int* s_kee
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       if (avail[i]) s_sig[lane + kWave * i] = sigmoid64((double)v[i]);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    wave_sync_lds();
     double score = -1.0;
     if (lane < p.n_group) {
       double b1 = -1.0, b2 = -1.0;
       for (int q = 0; q < gsize; ++q) {
-        double s = s_sig[lane * gsize + q];
-        if (s > b1) { b2 = b1; b1 = s; }
-        else if (s > b2) { b2 = s; }
+        double sg = s_sig[lane * gsize + q];
+        if (sg > b1) { b2 = b1; b1 = sg; }
+        else if (sg > b2) { b2 = sg; }
       }
       score = b1 + (gsize > 1 ? b2 : 0.0);
     }
+    wave_sync_lds();   // every lane is done with the sigmoids
+    if (lane < p.n_group) s_sig[lane] = score;
+    wave_sync_lds();
     // rank of my group: groups with a larger score, or an equal score and a lower index
     int rank = 0;
-    for (int g = 0; g < p.n_group; ++g) {
-      double o = __shfl(score, g, kWave);
-      rank += (o > score || (o == score && g < lane)) ? 1 : 0;
-    }
-    if (lane < p.n_group) s_keep[lane] = rank < p.topk_group ? 1 : 0;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (lane < p.n_group)
+      for (int g = 0; g < p.n_group; ++g) {
+        const double o = s_sig[g];
+        rank += (o > score || (o == score && g < lane)) ? 1 : 0;
+      }
+    const uint64_t keep = __ballot(lane < p.n_group && rank < p.topk_group);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      if (avail[i]) avail[i] = s_keep[(lane + kWave * i) / gsize] != 0;
+      if (avail[i]) avail[i] = (keep >> ((lane + kWave * i) / gsize)) & 1ull;
+    wave_sync_lds();   // the group scores are read; s_sig is free
   }
-
-  // softmax without renormalisation needs the full denominator
-  double full_den = 0.0;
-  double vmax_all = 0.0;
 
   int my_id = INT_MAX;
   float my_v = 0.f;
-  float first_v = 0.f;
-  for (int j = 0; j < p.k; ++j) {
-    float bv = 0.f;
-    int bi = INT_MAX;
+  float first_v;
+  int* s_id = s_keep;                   // selection j: expert, value
+  float* s_val = (float*)(s_keep + 16);
+  if (p.E <= 2 * kWave) {
+    // rank = number of available experts with a larger key
+    uint64_t* keys = (uint64_t*)s_sig;
+    const int epad = (p.E + 15) & ~15;
+    uint64_t kown[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int e = lane + kWave * i;
-      if (avail[i] && better(v[i], e, bv, bi)) { bv = v[i]; bi = e; }
+    for (int i = 0; i < 2; ++i) {
+      const int e = lane + kWave * i;
+      kown[i] = avail[i] ? order_key(v[i], e) : 0ull;
+      if (e < epad) keys[e] = kown[i];
+    }
+    wave_sync_lds();
+    int rank[2] = {0, 0};
+    for (int e0 = 0; e0 < epad; e0 += 16) {
+      uint64_t c[16];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const ulonglong2 two = *(const ulonglong2*)(keys + e0 + 2 * q);
+        c[2 * q] = two.x;
+        c[2 * q + 1] = two.y;
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        rank[0] += c[u] > kown[0] ? 1 : 0;
+        rank[1] += c[u] > kown[1] ? 1 : 0;
+      }
     }
 #pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) {
-      float ov = __shfl_xor(bv, off, kWave);
-      int oi = __shfl_xor(bi, off, kWave);
-      if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+    for (int i = 0; i < 2; ++i)
+      if (avail[i] && rank[i] < p.k) {
+        s_id[rank[i]] = lane + kWave * i;
+        s_val[rank[i]] = v[i];
+      }
+    wave_sync_lds();
+    if (lane < p.k) {
+      my_id = s_id[lane];
+      my_v = s_val[lane];
     }
-    if (j == 0) first_v = bv;
-    if (lane == j) { my_id = bi; my_v = bv; }
-    if (bi != INT_MAX && (bi & (kWave - 1)) == lane) {
+    first_v = s_val[0];
+  } else {
+    for (int j = 0; j < p.k; ++j) {
+      float bv = 0.f;
+      int bi = INT_MAX;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (bi == lane + kWave * i) avail[i] = false;
+      for (int i = 0; i < 4; ++i) {
+        int e = lane + kWave * i;
+        if (avail[i] && better(v[i], e, bv, bi)) { bv = v[i]; bi = e; }
+      }
+#pragma unroll
+      for (int off = kWave / 2; off > 0; off >>= 1) {
+        float ov = __shfl_xor(bv, off, kWave);
+        int oi = __shfl_xor(bi, off, kWave);
+        if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+      }
+      if (lane == j) { my_id = bi; my_v = bv; }
+      if (lane == 0 && j == 0) s_val[0] = bv;   // the first selection's value
+      if (bi != INT_MAX && (bi & (kWave - 1)) == lane) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (bi == lane + kWave * i) avail[i] = false;
+      }
     }
+    wave_sync_lds();
+    first_v = s_val[0];
   }
 
+  // weights in fp64; the k terms of a renormalisation are added in selection
+  // order
+  double* s_term = s_sig;
+  auto sum_k = [&](double term) {
+    if (lane < p.k) s_term[lane] = term;
+    wave_sync_lds();
+    double den = 0.0;
+    for (int j = 0; j < p.k; ++j) den += s_term[j];
+    return den;
+  };
   double wj;
   if (p.scoring == 0) {
     if (p.renorm) {
-      double ex = lane < p.k ? exp((double)my_v - (double)first_v) : 0.0;
-      wj = ex / wave_sum(ex);
+      const double ex = lane < p.k ? exp((double)my_v - (double)first_v) : 0.0;
+      wj = ex / sum_k(ex);
     } else {
-      // max over all experts: the first selection when nothing is masked
-      float m = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (lane + kWave * i < p.E) m = fmaxf(m, v[i]);
-#pragma unroll
-      for (int off = kWave / 2; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
-      vmax_all = (double)m;
+      // nothing is masked (grouping needs sigmoid scoring): the first
+      // selection is the maximum over all experts
+      const double vmax_all = (double)first_v;
       double part = 0.0;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         if (lane + kWave * i < p.E) part += exp((double)v[i] - vmax_all);
-      full_den = wave_sum(part);
+      const double full_den = wave_sum(part);
       wj = exp((double)my_v - vmax_all) / full_den;
     }
   } else {
-    double sg = lane < p.k ? sigmoid64((double)my_v) : 0.0;
-    wj = p.renorm ? sg / wave_sum(sg) : sg;
+    const double sg = lane < p.k ? sigmoid64((double)my_v) : 0.0;
+    wj = p.renorm ? sg / sum_k(sg) : sg;
   }
   *out_id = my_id;
   *out_w = (float)(wj * (double)p.scale);
