@@ -88,22 +88,45 @@ __device__ __forceinline__ uint64_t order_key(float f, int e) {
   return ((uint64_t)u << 32) | (uint64_t)(0xffffffffu - (unsigned)e);
 }
 
-// rank[i] += number of keys in row[0, n) above kown[i], for the NV own values.
-template <int NV>
-__device__ __forceinline__ void rank_keys(const uint64_t* row, int n, const uint64_t* kown,
-                                          int* rank) {
-  for (int e0 = 0; e0 < n; e0 += 16) {
-    uint64_t c[16];
+// Top-k of one token's keys by the calling wave (NV keys per lane, lane l
+// holding experts l, l + 64, ...; key 0 = not selectable).  The k largest
+// keys lie in the lanes whose own largest key is among the k largest lane
+// maxima, so the lane maxima are ranked first (64 compares per lane), those k
+// lanes write their NV keys as NV * k candidates, and each candidate is ranked
+// among the candidates alone: every key above a top-k key is a top-k key too,
+// so for rank < k this is the rank among all keys.  `wk` is per-wave LDS of at
+// least 64 + NV * k keys.  Calls sel(i, rank) for each own key i of rank < k.
+template <int NV, typename Sel>
+__device__ __forceinline__ void wave_topk(uint64_t* wk, const uint64_t* kown, int lane, int k,
+                                          Sel sel) {
+  uint64_t lm = kown[0];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const ulonglong2 two = *(const ulonglong2*)(row + e0 + 2 * q);
-      c[2 * q] = two.x;
-      c[2 * q + 1] = two.y;
+  for (int i = 1; i < NV; ++i) lm = kown[i] > lm ? kown[i] : lm;
+  wk[lane] = lm;
+  wave_sync_lds();
+  int lr = 0;
+#pragma unroll
+  for (int c = 0; c < 64; c += 2) {
+    const ulonglong2 two = *(const ulonglong2*)(wk + c);
+    lr += (two.x > lm ? 1 : 0) + (two.y > lm ? 1 : 0);
+  }
+  uint64_t* cand = wk + 64;
+  if (lr < k)
+#pragma unroll
+    for (int i = 0; i < NV; ++i) cand[lr * NV + i] = kown[i];
+  wave_sync_lds();
+  if (lr < k) {
+    int r[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) r[i] = 0;
+    for (int c = 0; c < NV * k; ++c) {
+      const uint64_t o = cand[c];
+#pragma unroll
+      for (int i = 0; i < NV; ++i) r[i] += o > kown[i] ? 1 : 0;
     }
 #pragma unroll
-    for (int u = 0; u < 16; ++u)
-#pragma unroll
-      for (int i = 0; i < NV; ++i) rank[i] += c[u] > kown[i] ? 1 : 0;
+    for (int i = 0; i < NV; ++i)
+      if (kown[i] != 0ull && r[i] < k) sel(i, r[i]);
   }
 }
 
@@ -140,7 +163,6 @@ __device__ void route_prologue(const GemvParams& p, RouteLdsT<NW>& L, int blk, b
   const int wave = tid >> 6;
   const int T = p.T, E = p.E, k = p.k;
   const int n = T * k;
-  const int Epad = (E + 15) & ~15;
 
   for (int e = tid; e < E; e += nthr) L.tokmask[e] = 0u;
   if (tid < 16) L.rowslot[tid] = -1;
@@ -193,34 +215,27 @@ __device__ void route_prologue(const GemvParams& p, RouteLdsT<NW>& L, int blk, b
         if (e < E && !((keep_mask >> (e / gsize)) & 1ull)) v[i] = -INFINITY;
       }
     }
-    // rank = number of experts whose key is larger: keys order by logit, then
-    // by lower expert index; masked experts have key 0 and beat nobody
+    // the k largest keys: keys order by logit, then by lower expert index;
+    // masked experts have key 0 and are never selected
     uint64_t kown[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = lane + 64 * i;
       kown[i] = (e < E && v[i] != -INFINITY) ? order_key(v[i], e) : 0ull;
-      if (e < Epad) wk[e] = kown[i];
     }
-    wave_sync_lds();
-    int rank[4] = {0, 0, 0, 0};
+    auto sel = [&](int i, int r) {
+      L.ids[t * k + r] = lane + 64 * i;
+      L.val[t * k + r] = v[i];
+    };
     const int nv = (E + 63) >> 6;
     if (nv == 1)
-      rank_keys<1>(wk, Epad, kown, rank);
+      wave_topk<1>(wk, kown, lane, k, sel);
     else if (nv == 2)
-      rank_keys<2>(wk, Epad, kown, rank);
+      wave_topk<2>(wk, kown, lane, k, sel);
     else if (nv == 3)
-      rank_keys<3>(wk, Epad, kown, rank);
+      wave_topk<3>(wk, kown, lane, k, sel);
     else
-      rank_keys<4>(wk, Epad, kown, rank);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = lane + 64 * i;
-      if (e < E && v[i] != -INFINITY && rank[i] < k) {
-        L.ids[t * k + rank[i]] = e;
-        L.val[t * k + rank[i]] = v[i];
-      }
-    }
+      wave_topk<4>(wk, kown, lane, k, sel);
     wave_sync_lds();
     // weights in fp64: each selected lane forms its term, then sums the k terms
     // of the token in selection order
