@@ -38,6 +38,7 @@
 #include <limits.h>
 
 #include "moe_internal.h"
+#include "wave_topk.h"
 
 namespace moe {
 
@@ -64,12 +65,6 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-__device__ __forceinline__ void wave_sync_lds() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-}
-
 __device__ __forceinline__ double wave_sum(double v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
@@ -78,57 +73,6 @@ __device__ __forceinline__ double wave_sum(double v) {
 
 // ------------------------------------------------------------------ routing prologue
 constexpr int kRow = kMaxExperts;   // LDS row of one token's logits, padded with -inf
-
-// 64-bit key whose unsigned order is (logit descending-equal ..., lower index
-// first): high word = order-preserving image of the float (-0 folded into +0,
-// so the two compare equal as floats do), low word = inverted expert index.
-__device__ __forceinline__ uint64_t order_key(float f, int e) {
-  unsigned u = __float_as_uint(f + 0.0f);
-  u ^= (unsigned)((int)u >> 31) | 0x80000000u;
-  return ((uint64_t)u << 32) | (uint64_t)(0xffffffffu - (unsigned)e);
-}
-
-// Top-k of one token's keys by the calling wave (NV keys per lane, lane l
-// holding experts l, l + 64, ...; key 0 = not selectable).  The k largest
-// keys lie in the lanes whose own largest key is among the k largest lane
-// maxima, so the lane maxima are ranked first (64 compares per lane), those k
-// lanes write their NV keys as NV * k candidates, and each candidate is ranked
-// among the candidates alone: every key above a top-k key is a top-k key too,
-// so for rank < k this is the rank among all keys.  `wk` is per-wave LDS of at
-// least 64 + NV * k keys.  Calls sel(i, rank) for each own key i of rank < k.
-template <int NV, typename Sel>
-__device__ __forceinline__ void wave_topk(uint64_t* wk, const uint64_t* kown, int lane, int k,
-                                          Sel sel) {
-  uint64_t lm = kown[0];
-#pragma unroll
-  for (int i = 1; i < NV; ++i) lm = kown[i] > lm ? kown[i] : lm;
-  wk[lane] = lm;
-  wave_sync_lds();
-  int lr = 0;
-#pragma unroll
-  for (int c = 0; c < 64; c += 2) {
-    const ulonglong2 two = *(const ulonglong2*)(wk + c);
-    lr += (two.x > lm ? 1 : 0) + (two.y > lm ? 1 : 0);
-  }
-  uint64_t* cand = wk + 64;
-  if (lr < k)
-#pragma unroll
-    for (int i = 0; i < NV; ++i) cand[lr * NV + i] = kown[i];
-  wave_sync_lds();
-  if (lr < k) {
-    int r[NV];
-#pragma unroll
-    for (int i = 0; i < NV; ++i) r[i] = 0;
-    for (int c = 0; c < NV * k; ++c) {
-      const uint64_t o = cand[c];
-#pragma unroll
-      for (int i = 0; i < NV; ++i) r[i] += o > kown[i] ? 1 : 0;
-    }
-#pragma unroll
-    for (int i = 0; i < NV; ++i)
-      if (kown[i] != 0ull && r[i] < k) sel(i, r[i]);
-  }
-}
 
 constexpr int kPrologueWaves = 4;     // waves of GEMV1, which carries the prologue
 constexpr int kRouteWaves = 16;       // waves of the route kernel: one per token
@@ -227,15 +171,7 @@ __device__ void route_prologue(const GemvParams& p, RouteLdsT<NW>& L, int blk, b
       L.ids[t * k + r] = lane + 64 * i;
       L.val[t * k + r] = v[i];
     };
-    const int nv = (E + 63) >> 6;
-    if (nv == 1)
-      wave_topk<1>(wk, kown, lane, k, sel);
-    else if (nv == 2)
-      wave_topk<2>(wk, kown, lane, k, sel);
-    else if (nv == 3)
-      wave_topk<3>(wk, kown, lane, k, sel);
-    else
-      wave_topk<4>(wk, kown, lane, k, sel);
+    wave_topk_n((E + 63) >> 6, wk, kown, lane, k, sel);
     wave_sync_lds();
     // weights in fp64: each selected lane forms its term, then sums the k terms
     // of the token in selection order

@@ -7,7 +7,8 @@
 // BLOCK_M, pads marked with a value >= num_valid (*Common Pitfalls* 2).
 //
 // gfx950 design: one wave64 per token for gating (logits of up to 256 experts
-// live in four registers per lane; k rounds of a butterfly arg-max).  Align
+// live in four registers per lane; the top-k is a two-level rank of 64-bit
+// order keys through LDS).  Align
 // ranks slots inside a wave with ballots (the lanes holding the same expert
 // are found by AND-ing one ballot per bit of the expert id), combines waves
 // with a per-expert prefix in LDS, and is stable: slots of one expert keep
@@ -16,19 +17,13 @@
 #include <limits.h>
 
 #include "moe_internal.h"
+#include "wave_topk.h"
 
 namespace moe {
 
 namespace {
 
 constexpr int kWave = 64;
-
-__device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
-  // key order: larger logit first, lower expert index on ties; ib == INT_MAX is "none"
-  if (ib == INT_MAX) return ia != INT_MAX;
-  if (ia == INT_MAX) return false;
-  return va > vb || (va == vb && ia < ib);
-}
 
 __device__ __forceinline__ double wave_sum(double v) {
 #pragma unroll
@@ -38,28 +33,11 @@ __device__ __forceinline__ double wave_sum(double v) {
 
 __device__ __forceinline__ double sigmoid64(double l) { return 1.0 / (1.0 + exp(-l)); }
 
-// 64-bit key whose unsigned order is the selection order: high word = an
-// order-preserving image of the logit (-0 folded into +0, so the two compare
-// equal as floats do), low word = the inverted expert index (ties to the
-// lower index).  0 is below every key of an expert.
-__device__ __forceinline__ uint64_t order_key(float f, int e) {
-  unsigned u = __float_as_uint(f + 0.0f);
-  u ^= (unsigned)((int)u >> 31) | 0x80000000u;
-  return ((uint64_t)u << 32) | (uint64_t)(0xffffffffu - (unsigned)e);
-}
-
-// LDS writes of this wave visible to its other lanes
-__device__ __forceinline__ void wave_sync_lds() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 // Gating of token t by the calling wave.  `s_sig` is per-wave LDS scratch of
 // MOE_MAX_EXPERTS doubles, `s_keep` per-wave scratch of 64 ints.  Returns
 // through lane j < k: *out_id, *out_w.  Ranks and sums go through LDS (one
-// broadcast read per value) rather than chains of cross-lane shuffles; with
-// more than 128 experts the top-k is k rounds of a butterfly arg-max.
+// broadcast read per value) rather than chains of cross-lane shuffles; the
+// top-k is the two-level wave_topk.
 __device__ void gate_token(const GateParams& p, int t, double* s_sig, int* s_keep,
                            int* out_id, float* out_w) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -108,76 +86,25 @@ __device__ void gate_token(const GateParams& p, int t, double* s_sig, int* s_kee
     wave_sync_lds();   // the group scores are read; s_sig is free
   }
 
+  // the k largest keys (masked and absent experts have key 0); selection j's
+  // expert and value go to LDS slot j
+  int* s_id = s_keep;
+  float* s_val = (float*)(s_keep + 16);
+  uint64_t kown[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) kown[i] = avail[i] ? order_key(v[i], lane + kWave * i) : 0ull;
+  wave_topk_n((p.E + kWave - 1) / kWave, (uint64_t*)s_sig, kown, lane, p.k, [&](int i, int r) {
+    s_id[r] = lane + kWave * i;
+    s_val[r] = v[i];
+  });
+  wave_sync_lds();
   int my_id = INT_MAX;
   float my_v = 0.f;
-  float first_v;
-  int* s_id = s_keep;                   // selection j: expert, value
-  float* s_val = (float*)(s_keep + 16);
-  if (p.E <= 2 * kWave) {
-    // rank = number of available experts with a larger key
-    uint64_t* keys = (uint64_t*)s_sig;
-    const int epad = (p.E + 15) & ~15;
-    uint64_t kown[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int e = lane + kWave * i;
-      kown[i] = avail[i] ? order_key(v[i], e) : 0ull;
-      if (e < epad) keys[e] = kown[i];
-    }
-    wave_sync_lds();
-    int rank[2] = {0, 0};
-    for (int e0 = 0; e0 < epad; e0 += 16) {
-      uint64_t c[16];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const ulonglong2 two = *(const ulonglong2*)(keys + e0 + 2 * q);
-        c[2 * q] = two.x;
-        c[2 * q + 1] = two.y;
-      }
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        rank[0] += c[u] > kown[0] ? 1 : 0;
-        rank[1] += c[u] > kown[1] ? 1 : 0;
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      if (avail[i] && rank[i] < p.k) {
-        s_id[rank[i]] = lane + kWave * i;
-        s_val[rank[i]] = v[i];
-      }
-    wave_sync_lds();
-    if (lane < p.k) {
-      my_id = s_id[lane];
-      my_v = s_val[lane];
-    }
-    first_v = s_val[0];
-  } else {
-    for (int j = 0; j < p.k; ++j) {
-      float bv = 0.f;
-      int bi = INT_MAX;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        int e = lane + kWave * i;
-        if (avail[i] && better(v[i], e, bv, bi)) { bv = v[i]; bi = e; }
-      }
-#pragma unroll
-      for (int off = kWave / 2; off > 0; off >>= 1) {
-        float ov = __shfl_xor(bv, off, kWave);
-        int oi = __shfl_xor(bi, off, kWave);
-        if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-      }
-      if (lane == j) { my_id = bi; my_v = bv; }
-      if (lane == 0 && j == 0) s_val[0] = bv;   // the first selection's value
-      if (bi != INT_MAX && (bi & (kWave - 1)) == lane) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (bi == lane + kWave * i) avail[i] = false;
-      }
-    }
-    wave_sync_lds();
-    first_v = s_val[0];
+  if (lane < p.k) {
+    my_id = s_id[lane];
+    my_v = s_val[lane];
   }
+  const float first_v = s_val[0];
 
   // weights in fp64; the k terms of a renormalisation are added in selection
   // order
