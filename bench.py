@@ -48,8 +48,8 @@ DOMINANT_TRAFFIC = {
     "src": "grouped_gemm_topk_amd/csrc/gemm.hip",
     "sha256": "8b242f9c6c16fe1b1214bd83aacff7c589522fba844da60620d4b72102b7bca0",
     "config": "dsv3",
-    "fetch_bytes": 1267778112,
-    "write_bytes": 89790682,
+    "fetch_bytes": 1269855552,
+    "write_bytes": 89791562,
 }
 
 
