@@ -839,7 +839,12 @@ __global__ void __launch_bounds__(kWaves * 64) decode_kernel(GemvParams p, int g
 }  // namespace
 
 // Tiles per workgroup: the largest power of two (up to the wave count) that
-// still leaves about two workgroups per CU; the remaining waves split K.
+// still leaves at least `target` workgroups; the remaining waves split K.
+// Measured targets: 768 for the W13 GEMV (about three workgroups per CU),
+// 384 for W2 (fatter workgroups: decode T = 1 27.4 -> 26.8 us, relu2 T = 1
+// 35.0 -> 33.8 us; 192 was slower again).
+constexpr int64_t kTilesTargetW13 = 768;
+constexpr int64_t kTilesTargetW2 = 384;
 static int pick_tiles(int64_t tiles, int waves, int64_t target) {
   int nt = 1;
   while (nt < waves && tiles / (2 * nt) >= target) nt *= 2;
@@ -851,8 +856,8 @@ static hipError_t launch_gemv_fmt(GemvParams p, bool swiglu, hipStream_t s) {
   const int nb = p.nblk + (p.sw13 ? 1 : 0);
   const int tiles1 = (p.I + 15) / 16;
   const int tiles2 = (p.H + 15) / 16;
-  p.nt1 = pick_tiles((int64_t)tiles1 * nb, swiglu ? kG1Waves / 2 : kG1Waves, 768);
-  p.nt2 = pick_tiles((int64_t)tiles2 * nb, kG2Waves, 768);
+  p.nt1 = pick_tiles((int64_t)tiles1 * nb, swiglu ? kG1Waves / 2 : kG1Waves, kTilesTargetW13);
+  p.nt2 = pick_tiles((int64_t)tiles2 * nb, kG2Waves, kTilesTargetW2);
   const int g1x = (tiles1 + p.nt1 - 1) / p.nt1;
   const int g2x = (tiles2 + p.nt2 - 1) / p.nt2;
   if (p.T * p.k >= kFusedMinSlots) {
