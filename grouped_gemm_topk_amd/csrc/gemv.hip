@@ -173,33 +173,38 @@ __device__ void route_prologue(const GemvParams& p, RouteLdsT<NW>& L, int blk, b
     };
     wave_topk_n((E + 63) >> 6, wk, kown, lane, k, sel);
     wave_sync_lds();
-    // weights in fp64: each selected lane forms its term, then sums the k terms
-    // of the token in selection order
-    double full = 0.0;
-    if (p.scoring == 0 && !p.renorm) {
-      const double m = (double)L.val[t * k];   // nothing is masked: the global max
-      double part = 0.0;
+    // weights in fp64 (only where the routing outputs are written: the GEMV
+    // reads them from there): each selected lane forms its term, then sums
+    // the k terms of the token in selection order
+    if (write_out) {
+      double full = 0.0;
+      if (p.scoring == 0 && !p.renorm) {
+        const double m = (double)L.val[t * k];   // nothing is masked: the global max
+        double part = 0.0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (lane + 64 * i < E) part += exp((double)v[i] - m);
-      full = wave_sum(part);
-    }
-    double term = 0.0;
-    if (lane < k) {
-      const double mine = (double)L.val[t * k + lane];
-      term = p.scoring == 0 ? exp(mine - (double)L.val[t * k]) : 1.0 / (1.0 + exp(-mine));
-      L.ex[t * k + lane] = term;
-    }
-    wave_sync_lds();
-    if (lane < k) {
-      double den;
-      if (!p.renorm) {
-        den = p.scoring == 0 ? full : 1.0;
-      } else {
-        den = 0.0;
-        for (int j = 0; j < k; ++j) den += L.ex[t * k + j];
+        for (int i = 0; i < 4; ++i)
+          if (lane + 64 * i < E) part += exp((double)v[i] - m);
+        full = wave_sum(part);
       }
-      L.wts[t * k + lane] = (float)(term / den * (double)p.scale);
+      double term = 0.0;
+      if (lane < k) {
+        const double mine = (double)L.val[t * k + lane];
+        term = p.scoring == 0 ? exp(mine - (double)L.val[t * k]) : 1.0 / (1.0 + exp(-mine));
+        L.ex[t * k + lane] = term;
+      }
+      wave_sync_lds();
+      if (lane < k) {
+        double den;
+        if (!p.renorm) {
+          den = p.scoring == 0 ? full : 1.0;
+        } else {
+          den = 0.0;
+          for (int j = 0; j < k; ++j) den += L.ex[t * k + j];
+        }
+        L.wts[t * k + lane] = (float)(term / den * (double)p.scale);
+      }
+    }
+    if (lane < k) {
       atomicOr(&L.tokmask[L.ids[t * k + lane]], 1u << t);
     }
   }
