@@ -211,33 +211,25 @@ __device__ void route_prologue(const GemvParams& p, RouteLdsT<NW>& L, int blk, b
   __syncthreads();
 
   // ---- align: count of expert e = popcount(tokmask[e]); the rank of token t's
-  // slot inside expert e = tokens below t that picked e (slots ascend with t)
+  // slot inside expert e = tokens below t that picked e (slots ascend with t).
+  // An expert holds at most T <= 16 <= bm slots, so its padded count is 0 or
+  // bm: its offset is bm times the number of non-empty experts below it (one
+  // ballot per 64 experts), and it owns at most one block.
   if (tid < 64) {
-    int pc[4], local = 0;
+    int before = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      int e = tid * 4 + i;
-      int c = e < E ? __popc(L.tokmask[e]) : 0;
-      pc[i] = (c + p.bm - 1) / p.bm * p.bm;
-      local += pc[i];
-    }
-    int incl = local;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      int u = __shfl_up(incl, o, 64);
-      if (tid >= o) incl += u;
-    }
-    int run = incl - local;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int e = tid * 4 + i;
+      const int e = tid + 64 * i;
+      const bool ne = e < E && L.tokmask[e] != 0u;
+      const uint64_t m = __ballot(ne);
+      const int idx = before + __popcll(m & ((1ull << tid) - 1ull));
       if (e < E) {
-        L.off[e] = run;
-        if (pc[i] > 0) L.blk_expert[run / p.bm] = e;   // one block per expert (c <= 16 <= bm)
+        L.off[e] = idx * p.bm;
+        if (ne) L.blk_expert[idx] = e;
       }
-      run += pc[i];
+      before += __popcll(m);
     }
-    if (tid == 63) L.ntpp = incl;
+    if (tid == 0) L.ntpp = before * p.bm;
   }
   __syncthreads();
   const int ntpp = L.ntpp;
