@@ -46,7 +46,7 @@ DECODE_CASES = ("decode_t1", "decode_t3", "decode_t8", "relu2_t1", "relu2_t16")
 # digest; any other source reports traffic null until it is measured again.
 DOMINANT_TRAFFIC = {
     "src": "grouped_gemm_topk_amd/csrc/gemm.hip",
-    "sha256": "8b242f9c6c16fe1b1214bd83aacff7c589522fba844da60620d4b72102b7bca0",
+    "sha256": "f3cf547573cf7b2a97d86d1a33e96e430c6eff36a79dfa04a6dbdf1ade23c868",
     "config": "dsv3",
     "fetch_bytes": 1269855552,
     "write_bytes": 89791562,

@@ -37,6 +37,7 @@
 // v_mfma_f32_16x16x32_bf16 for BLOCK_M = 16.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "moe_internal.h"
@@ -698,18 +699,19 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) grouped_gemm_ker
 #undef MOE_VMW
 }
 
-// compute units of the current device (cached per device; 0 if unknown)
+// compute units of the current device (cached per device, safe to call from
+// several host threads; 0 if unknown)
 int cu_count() {
   constexpr int kMaxDev = 64;
-  static int cache[kMaxDev];
+  static std::atomic<int> cache[kMaxDev];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 0;
-  if (cache[dev] == 0) {
-    int n = 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    cache[dev] = n;
+    cache[dev].store(n, std::memory_order_relaxed);
   }
-  return cache[dev];
+  return n;
 }
 
 template <int BM, int BNW, int WAVES_M, int WAVES_N, int BK, int NS, int MINW>
