@@ -48,8 +48,8 @@ DOMINANT_TRAFFIC = {
     "src": "grouped_gemm_topk_amd/csrc/gemm.hip",
     "sha256": "f3cf547573cf7b2a97d86d1a33e96e430c6eff36a79dfa04a6dbdf1ade23c868",
     "config": "dsv3",
-    "fetch_bytes": 1269855552,
-    "write_bytes": 89791562,
+    "fetch_bytes": 1320452160,
+    "write_bytes": 89789088,
 }
 
 
