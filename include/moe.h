@@ -20,8 +20,8 @@
  * - The caller owns every buffer, including the workspace.  The library never
  *   allocates device memory, never synchronises the stream and never copies to
  *   the host.  All work is enqueued asynchronously on `stream`.
- * - Workspace (moe_align, moe_fused_forward): `workspace_bytes` must not be
- *   NULL.  With `workspace == NULL` the call only writes the required byte
+ * - Workspace (moe_align, moe_grouped_gemm_backward and the moe_fused_forward
+ *   family): `workspace_bytes` must not be NULL.  With `workspace == NULL` the call only writes the required byte
  *   count (possibly 0) to `*workspace_bytes` and launches nothing; call again
  *   with a non-NULL buffer of at least that many bytes and its size in
  *   `*workspace_bytes`.  moe_grouped_gemm needs no workspace and ignores both
