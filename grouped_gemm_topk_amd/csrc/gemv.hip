@@ -646,6 +646,10 @@ __global__ void __launch_bounds__(kG2Waves * 64) gemv2_kernel(GemvParams p) {
 
 // ------------------------------------------------------------------ fused path (larger T)
 constexpr int kWaves = kPrologueWaves;   // waves of every decode workgroup
+// the launcher sizes the tiles per workgroup of both decode forms with the
+// GEMV wave counts, so the fused kernel must have the same waves (each tile's
+// waves split K: kWaves / tiles per workgroup >= 1)
+static_assert(kWaves == kG1Waves && kWaves == kG2Waves, "decode wave counts must agree");
 // slots (T * top_k) from which the fused path runs: measured on MI355X, the
 // separate W2 launch is cheaper at 8 and 24 slots (128 experts top-8, T = 1, 3
 // and top-6, T = 1), the fused launch at 64 and 96 (T = 8 top-8, T = 16 top-6)
