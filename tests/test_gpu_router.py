@@ -102,3 +102,39 @@ def test_router_layer_full_size(moe, name):
         want = O.token_output(inp, int(t), ids[t], wts[t], cfg.activation, cfg.n_shared)
         err = np.abs(got[t] - want).max()
         assert err <= 2e-2, f"token {t}: max|d|={err:.3g}"
+
+
+@pytest.mark.parametrize("cfg", [
+    W.small_config("rt_graph_prefill", T=70, H=128, I=64, E=18, top_k=4, scoring=W.SCORE_SIGMOID,
+                   n_group=6, topk_group=4, n_shared=1, block_m=32),
+    W.small_config("rt_graph_decode", T=3, H=256, I=128, E=64, top_k=8),
+], ids=["prefill", "decode"])
+def test_router_layer_graph_replays(moe, cfg):
+    """The router-fused layer captured once and replayed with eager work in
+    between: every replay within fp32 reassociation of the eager result."""
+    inp = W.make_inputs(cfg)
+    p = moe.LayerParams.from_config(cfg)
+    sh = [to_dev(inp["shared_w13"]), to_dev(inp["shared_w2"])] if cfg.n_shared else [None, None]
+    layer = moe.FusedLayer(p, to_dev(inp["x"]), None, to_dev(inp["w13"]), to_dev(inp["w2"]), *sh,
+                           router_w=to_dev(W.make_router_weight(cfg)))
+    eager = layer.run().clone()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layer.run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        out = layer.run()
+    torch.cuda.synchronize()
+    want = eager.cpu().numpy()
+    for rep in range(3):
+        layer.tensors["out"].fill_(float("nan"))
+        if rep == 1:
+            layer.run()
+        g.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_allclose(out.cpu().numpy(), want, rtol=1e-5,
+                                   atol=1e-6 * np.abs(want).max(), err_msg=f"replay {rep}")
