@@ -206,3 +206,43 @@ def test_indexed_grouped_gemm_backward_full_size_sampled(moe, sc):
     gw = np.stack([dw[e, n].float().cpu().numpy() for e, n in wrows])
     assert not (np.abs(gx - sx) > _tol(sx, False)).any(), f"dx worst {np.abs(gx - sx).max()}"
     assert not (np.abs(gw - sw) > _tol(sw, False)).any(), f"dw worst {np.abs(gw - sw).max()}"
+
+
+def test_indexed_grouped_gemm_backward_graph_replays(moe):
+    """align + backward (dx, dw) captured once and replayed with eager work in
+    between: every replay equals the eager result bit for bit (the layout
+    kernels and the GEMMs are deterministic)."""
+    sc = W.small_gemm_scenario("cg_bwd_graph", G=5, M=900, N=264, K=200, sizes=(0, 400, 1, 250, 249),
+                               block_m=64)
+    inp = W.make_gemm_inputs(sc, with_grad=True)
+    op = moe.IndexedGroupedGemm(to_dev(inp["x"]), to_dev(inp["w"]), to_dev(inp["expert_indices"]),
+                                sc.block_m)
+    dy = to_dev(inp["dy"])
+    dx = torch.empty((sc.M, sc.K), dtype=torch.bfloat16, device="cuda")
+    dw = torch.empty((sc.G, sc.N, sc.K), dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        op.align()
+        op.backward(dy, dx, dw)
+
+    step()
+    torch.cuda.synchronize()
+    ex, ew = dx.clone(), dw.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        dx.fill_(float("nan"))
+        dw.fill_(float("nan"))
+        if rep == 1:
+            step()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(dx, ex) and torch.equal(dw, ew), f"replay {rep}"
