@@ -202,9 +202,9 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) grouped_gemm_ker
   const int G = gridDim.x;
   const int ncols = SW ? pin.I : pin.N;   // output columns
   constexpr int GM = MOE_GM;
-  // kNoRow: an offset beyond every descriptor even after the K advance is
-  // added, so the load reads zeros
-  constexpr int kNoRow = 0x7fff0000;
+  // kNoRow: an offset beyond every descriptor (the host keeps operand buffers
+  // below it) even after the K advance is added, so the load reads zeros
+  constexpr int kNoRow = kNoRowOffset;
 
   // the expert ids of the routed m-blocks, copied to LDS once per workgroup
   // (every tile's mapping reads them) when the tile's LDS leaves room

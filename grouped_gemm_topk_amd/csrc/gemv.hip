@@ -117,10 +117,12 @@ __device__ void route_prologue(const GemvParams& p, RouteLdsT<NW>& L, int blk, b
   uint64_t* wk = L.key[wave];
   for (int t = wave; t < T; t += NW) {
     float v[4];
+    bool avail[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       int e = lane + 64 * i;
-      v[i] = e < E ? p.logits[t * E + e] : -INFINITY;
+      avail[i] = e < E;
+      v[i] = avail[i] ? p.logits[t * E + e] : 0.f;
     }
     if (p.n_group > 1) {
       // groups of gsize contiguous experts ranked by the sum of their two
@@ -156,17 +158,15 @@ __device__ void route_prologue(const GemvParams& p, RouteLdsT<NW>& L, int blk, b
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         int e = lane + 64 * i;
-        if (e < E && !((keep_mask >> (e / gsize)) & 1ull)) v[i] = -INFINITY;
+        if (e < E && !((keep_mask >> (e / gsize)) & 1ull)) avail[i] = false;
       }
     }
     // the k largest keys: keys order by logit, then by lower expert index;
-    // masked experts have key 0 and are never selected
+    // absent and group-masked experts have key 0 and are never selected (a
+    // logit of -inf still has a non-zero key)
     uint64_t kown[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = lane + 64 * i;
-      kown[i] = (e < E && v[i] != -INFINITY) ? order_key(v[i], e) : 0ull;
-    }
+    for (int i = 0; i < 4; ++i) kown[i] = avail[i] ? order_key(v[i], lane + 64 * i) : 0ull;
     auto sel = [&](int i, int r) {
       L.ids[t * k + r] = lane + 64 * i;
       L.val[t * k + r] = v[i];

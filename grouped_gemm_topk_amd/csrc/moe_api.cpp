@@ -35,7 +35,9 @@ int check_device() {
   return st == 1 ? MOE_OK : MOE_ERR_DEVICE;
 }
 
-constexpr int64_t kMaxBufferBytes = (int64_t)1 << 31;
+// byte offsets inside one operand buffer are 32-bit, and the grouped GEMM's
+// masked loads use an offset at kNoRowOffset that must lie past the buffer
+constexpr int64_t kMaxBufferBytes = moe::kNoRowOffset;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }

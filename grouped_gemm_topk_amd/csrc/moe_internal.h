@@ -10,6 +10,12 @@ namespace moe {
 
 constexpr int kMaxExperts = 256;
 
+// The grouped GEMM's "no row" load offset: a masked load (pad row, ragged K
+// tail, columns past N) reads zeros because this offset lies at or beyond the
+// end of its buffer descriptor.  The host therefore accepts operand buffers
+// (token rows, activation rows, one expert's weights) of fewer bytes than this.
+constexpr int kNoRowOffset = 0x7fff0000;
+
 // ---------------------------------------------------------------- gating
 struct GateParams {
   const float* logits;  // [T, E]

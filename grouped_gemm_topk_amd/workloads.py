@@ -348,3 +348,60 @@ def make_router_weight(cfg: MoEConfig, layer: int = 0) -> np.ndarray:
     """bf16 bits [E, H] ~ N(0, w_std): the gate's weight, logits = x . W^T
     (the HF DeepSeek-V3 gate's linear layer, ``initializer_range``)."""
     return _normal_bf16((cfg.E, cfg.H), cfg.w_std, cfg.family, layer, _TID_ROUTER)
+
+
+# ---------------------------------------------------------------------------
+# router logits with exact ties (for the lower-index tie rule of top-k)
+# ---------------------------------------------------------------------------
+_TID_TIES = 9
+TIE_MODES = ("equal", "coarse", "signed_zero", "kth", "groups_equal", "groups_two")
+
+
+def make_tie_logits(T: int, E: int, k: int, mode: str, seed: int = 0,
+                    n_group: int = 1) -> np.ndarray:
+    """Router logits [T, E] float32 built so that many keys are exactly equal.
+
+    * ``equal``: every row constant (values from {-1.5, -0.0, +0.0, 0.5, 2});
+      all experts tie.
+    * ``coarse``: N(0, 1) rounded to multiples of 0.5; ties everywhere,
+      often across the k-th place.
+    * ``signed_zero``: a mix of +0.0 and -0.0 with a few +-1 entries; +0 and
+      -0 are equal keys.
+    * ``kth``: k-1 distinct leaders (4, 4.25, ...), then three experts at 3.0
+      competing for the k-th place, the rest N(0, 1) clipped to 2.5.
+    * ``groups_equal`` (n_group contiguous groups): every group holds a
+      permutation of one multiset of non-negative multiples of 0.5, so all
+      group scores are equal and equal values repeat across groups.
+    * ``groups_two``: two multisets, a clearly stronger one (values + 2) on a
+      random half of the groups; the groups of each multiset tie.
+    """
+    rng = _rng(200, T, E, k, seed, TIE_MODES.index(mode), _TID_TIES)
+    if mode == "equal":
+        vals = np.array([-1.5, -0.0, 0.0, 0.5, 2.0], np.float32)
+        return np.repeat(vals[rng.integers(0, vals.size, T)][:, None], E, axis=1)
+    if mode == "coarse":
+        return (np.round(rng.standard_normal((T, E)) * 2.0) / 2.0).astype(np.float32)
+    if mode == "signed_zero":
+        z = np.where(rng.random((T, E)) < 0.5, np.float32(-0.0), np.float32(0.0)).astype(np.float32)
+        few = rng.random((T, E)) < 0.05
+        z[few] = np.where(rng.random(few.sum()) < 0.5, -1.0, 1.0).astype(np.float32)
+        return z
+    if mode == "kth":
+        z = np.clip(rng.standard_normal((T, E)), -2.5, 2.5).astype(np.float32)
+        for t in range(T):
+            p = rng.permutation(E)
+            z[t, p[:k - 1]] = 4.0 + 0.25 * np.arange(k - 1, dtype=np.float32)
+            z[t, p[k - 1:k + 2]] = 3.0
+        return z
+    if mode in ("groups_equal", "groups_two"):
+        if n_group < 2 or E % n_group:
+            raise ValueError("group modes need E a multiple of n_group >= 2")
+        gs = E // n_group
+        z = np.empty((T, E), np.float32)
+        for t in range(T):
+            base = (rng.integers(0, 7, gs) * 0.5).astype(np.float32)
+            strong = rng.random(n_group) < 0.5 if mode == "groups_two" else np.zeros(n_group, bool)
+            for g in range(n_group):
+                z[t, g * gs:(g + 1) * gs] = rng.permutation(base) + (2.0 if strong[g] else 0.0)
+        return z
+    raise ValueError(f"unknown tie mode {mode!r}")

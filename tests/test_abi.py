@@ -161,6 +161,15 @@ def test_grouped_gemm_validation(L):
     assert call(epilogue=3, capacity=0) == 0   # scatter without weights is valid (weight 1)
     assert call(w=fake + 8) == -5
     assert call(capacity=0) == 0           # nothing to do
+    # operand buffers must stay below the kernel's masked-load offset
+    # (0x7fff0000 bytes): one expert's weights of 8 x K bf16 just past it, and
+    # an A operand of 2 x K bf16 rows just past it, are rejected
+    k_band = (0x7fff0000 // 16 + 8) // 8 * 8
+    assert 0x7fff0000 <= 16 * k_band < 1 << 31
+    assert call(N=8, K=k_band) == -4
+    k_a = (0x7fff0000 // 32 + 8) // 8 * 8            # 16 A rows of k_a bf16 in the band
+    assert 0x7fff0000 <= 32 * k_a < 1 << 31
+    assert call(a_row_div=1, num_valid=16, N=8, K=k_a) == -4
 
 
 def test_grouped_gemm_backward_validation_and_sizes(L):

@@ -50,6 +50,9 @@ def _check(cfg, inp, mx, got, r):
     nt = int(r["num_tokens_post_padded"].cpu().item())
     assert nt == ref["num_tokens_post_padded"]
     assert np.array_equal(r["sorted_token_ids"].cpu().numpy()[:nt], ref["sorted_token_ids"])
+    assert np.array_equal(r["expert_ids"].cpu().numpy()[:nt // cfg.block_m], ref["expert_ids"])
+    np.testing.assert_allclose(r["topk_weights"].cpu().numpy(), ref["topk_weights"], rtol=2e-6,
+                               atol=1e-7)
     want = ref["out"].astype(np.float64)
     err = np.abs(got.astype(np.float64) - want)
     rel = np.linalg.norm(got - want) / np.linalg.norm(want)

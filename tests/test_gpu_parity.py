@@ -220,22 +220,18 @@ def test_fused_forward_zero_tokens(moe):
 
 
 # ---------------------------------------------------------------- full-size configs
-def _full_case(moe, name, n_sample=None):
+def _full_case(moe, name):
+    """Every config at its full size in the launch configuration the benchmark
+    times: routing bit-exact and the whole [T, H] output against the oracle's
+    layer (a per-expert loop over all tokens)."""
     cfg = W.CONFIGS[name]
     print(f"full-size {name}", flush=True)
     inp = W.make_inputs(cfg)
-    # routing at full size from the oracle (cheap); the output on sampled tokens
-    ids, wts = O.gate(inp["logits"], cfg.top_k, cfg.scoring, cfg.n_group, cfg.topk_group,
-                      cfg.renormalize, cfg.scale)
-    ref = {"topk_ids": ids, "topk_weights": wts, **O.align(ids, cfg.E, cfg.block_m)}
     out, routing = _run_fused(moe, cfg, inp)
+    ref = O.moe_forward_cfg(cfg, inp)
     _check_routing(routing, ref, cfg.T, cfg.top_k, cfg.block_m)
-    rng = np.random.default_rng(5)
-    toks = np.arange(cfg.T) if n_sample is None or n_sample >= cfg.T else \
-        np.unique(np.concatenate([[0, cfg.T - 1], rng.choice(cfg.T, n_sample, replace=False)]))
-    want = np.stack([O.token_output(inp, int(t), ids[t], wts[t], cfg.activation, cfg.n_shared)
-                     for t in toks])
-    return assert_out_close(out[toks], want, name)
+    max_abs, rel = assert_out_close(out, ref["out"], name)
+    print(f"full-size {name}: max|d|={max_abs:.3g} rel-L2={rel:.3g}", flush=True)
 
 
 @pytest.mark.parametrize("name", ["decode_t1", "decode_t3", "decode_t8", "relu2_t1", "relu2_t16"])
@@ -243,7 +239,6 @@ def test_full_decode_configs(moe, name):
     _full_case(moe, name)
 
 
-@pytest.mark.parametrize("name,n", [("dsv3", 48), ("dsv3_s2.5", 48), ("zipf128", 48),
-                                    ("relu2_t2048", 48)])
-def test_full_prefill_configs_sampled(moe, name, n):
-    _full_case(moe, name, n)
+@pytest.mark.parametrize("name", ["dsv3", "dsv3_s2.5", "zipf128", "relu2_t2048"])
+def test_full_prefill_configs(moe, name):
+    _full_case(moe, name)
