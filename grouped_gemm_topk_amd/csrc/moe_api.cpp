@@ -14,6 +14,9 @@
 
 namespace {
 
+static_assert(MOE_NOALLOC_SCRATCH_BYTES == moe::kNoAllocScratchBytes,
+              "the header's scratch size is the library's");
+
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_dev_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
 
@@ -583,6 +586,28 @@ int moe_fused_forward(const moe_layer_params* p, const void* x, const float* rou
   return fused_forward(p, x, router_logits, false, nullptr, w13, w2, shared_w13, shared_w2, nullptr,
                        out, topk_ids, topk_weights, sorted_token_ids, expert_ids,
                        num_tokens_post_padded, workspace, workspace_bytes, stream);
+}
+
+int moe_fused_forward_noalloc(const moe_layer_params* p, const void* x,
+                              const float* router_logits, const void* w13, const void* w2,
+                              const void* shared_w13, const void* shared_w2, float* out,
+                              int32_t* topk_ids, float* topk_weights, int32_t* sorted_token_ids,
+                              int32_t* expert_ids, int32_t* num_tokens_post_padded,
+                              void* stream) {
+  int st = validate_layer(p);
+  if (st != MOE_OK) return st;
+  const size_t need = layout_layer(p, nullptr).bytes;
+  if (need > moe::kNoAllocScratchBytes) return MOE_ERR_CAPACITY;
+  if (p->T == 0) return MOE_OK;
+  st = check_device();
+  if (st != MOE_OK) return st;
+  void* ws = nullptr;
+  hipError_t e = moe::noalloc_scratch(&ws);
+  if (e != hipSuccess) return hip_status(e);
+  size_t bytes = moe::kNoAllocScratchBytes;
+  return fused_forward(p, x, router_logits, false, nullptr, w13, w2, shared_w13, shared_w2,
+                       nullptr, out, topk_ids, topk_weights, sorted_token_ids, expert_ids,
+                       num_tokens_post_padded, ws, &bytes, stream);
 }
 
 int moe_fused_forward_router(const moe_layer_params* p, const void* x, const void* router_w,

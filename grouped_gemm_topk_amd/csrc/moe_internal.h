@@ -142,6 +142,12 @@ hipError_t launch_gather_transpose(const uint16_t* src, int C, const int* sorted
 // (padded positions; both 0 for an expert without blocks)
 hipError_t launch_seg_table(const int* expert_ids, const int* ntpp, int block_m, int E,
                             int* seg_beg, int* seg_end, hipStream_t s);
+// The no-allocation entry point's workspace: a static device array of this
+// many bytes per GPU; *ptr = the current device's copy (its address is
+// looked up once per device).
+constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 hipError_t launch_combine(const float* yslot, int T, int k, int H, int has_shared, float* out,
                           hipStream_t s);
 

@@ -24,8 +24,10 @@ ACT_SWIGLU, ACT_RELU2 = 0, 1
 EPI_STORE, EPI_SWIGLU, EPI_RELU2, EPI_WEIGHTED_SCATTER = 0, 1, 2, 3
 
 EXPORTED = ("moe_align", "moe_grouped_gemm", "moe_grouped_gemm_backward", "moe_fused_forward",
-            "moe_fused_forward_mxfp8", "moe_fused_forward_router", "moe_align_capacity",
-            "moe_status_string")
+            "moe_fused_forward_mxfp8", "moe_fused_forward_router", "moe_fused_forward_noalloc",
+            "moe_align_capacity", "moe_status_string")
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 class MoeError(RuntimeError):
@@ -89,6 +91,9 @@ def lib() -> ctypes.CDLL:
         L.moe_fused_forward_router.argtypes = [ctypes.POINTER(MoeLayerParams), vp, vp, vp, vp, vp,
                                                vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moe_fused_forward_router.restype = ctypes.c_int
+        L.moe_fused_forward_noalloc.argtypes = [ctypes.POINTER(MoeLayerParams), vp, vp, vp, vp, vp,
+                                                vp, vp, vp, vp, vp, vp, vp, vp]
+        L.moe_fused_forward_noalloc.restype = ctypes.c_int
         L.moe_align_capacity.argtypes = [i32, i32, i32, i32]
         L.moe_align_capacity.restype = ctypes.c_int64
         L.moe_status_string.argtypes = [ctypes.c_int]
@@ -468,3 +473,44 @@ def moe_fused_forward(p: LayerParams, x, router_logits, w13, w2, shared_w13=None
     if p.T > 0:
         layer.run(stream)
     return (layer.out, layer.routing) if return_routing else layer.out
+
+
+def moe_fused_forward_noalloc(p: LayerParams, x, router_logits, w13, w2, shared_w13=None,
+                              shared_w2=None, out=None, routing=None, stream=None):
+    """The layer through moe_fused_forward_noalloc: no workspace, the library's
+    device-resident scratch instead (layers whose workspace exceeds it are
+    rejected).  ``out`` (fp32 [T, H]) and ``routing`` (a dict holding any of
+    topk_ids, topk_weights, sorted_token_ids, expert_ids,
+    num_tokens_post_padded) are caller tensors and are only checked here, so
+    that the call allocates nothing when they are given.  Returns ``out``."""
+    dev = x.device
+    _dev(x, "x", torch.bfloat16, (p.T, p.H))
+    _dev(router_logits, "router_logits", torch.float32, (p.T, p.E))
+    _dev(w13, "w13", torch.bfloat16, (p.E, p.M1, p.H))
+    _dev(w2, "w2", torch.bfloat16, (p.E, p.H, p.I))
+    if p.n_shared:
+        _dev(shared_w13, "shared_w13", torch.bfloat16, (p.M1, p.H))
+        _dev(shared_w2, "shared_w2", torch.bfloat16, (p.H, p.I))
+    if out is None:
+        out = torch.empty((p.T, p.H), dtype=torch.float32, device=dev)
+    _dev(out, "out", torch.float32, (p.T, p.H))
+    r = routing or {}
+    cap = align_capacity(p.T, p.top_k, p.E, p.block_m)
+    shapes = dict(topk_ids=(torch.int32, (p.T, p.top_k)),
+                  topk_weights=(torch.float32, (p.T, p.top_k)),
+                  sorted_token_ids=(torch.int32, None), expert_ids=(torch.int32, None),
+                  num_tokens_post_padded=(torch.int32, (1,)))
+    for name, t in r.items():
+        dt, shp = shapes[name]
+        _dev(t, name, dt, shp)
+    if "sorted_token_ids" in r and r["sorted_token_ids"].numel() < cap:
+        raise ValueError(f"sorted_token_ids needs {cap} entries")
+    if "expert_ids" in r and r["expert_ids"].numel() < max(cap // p.block_m, 1):
+        raise ValueError(f"expert_ids needs {max(cap // p.block_m, 1)} entries")
+    cp = p.c_struct()
+    _check("moe_fused_forward_noalloc", lib().moe_fused_forward_noalloc(
+        ctypes.byref(cp), _ptr(x), _ptr(router_logits), _ptr(w13), _ptr(w2), _ptr(shared_w13),
+        _ptr(shared_w2), _ptr(out), _ptr(r.get("topk_ids")), _ptr(r.get("topk_weights")),
+        _ptr(r.get("sorted_token_ids")), _ptr(r.get("expert_ids")),
+        _ptr(r.get("num_tokens_post_padded")), _stream(stream)))
+    return out

@@ -285,6 +285,28 @@ int moe_fused_forward_mxfp8(const moe_layer_params* p, const void* x, const floa
                             int32_t* num_tokens_post_padded, void* workspace,
                             size_t* workspace_bytes, void* stream);
 
+/*
+ * moe_fused_forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The library's own device-resident
+ * scratch array stands in for the workspace: MOE_NOALLOC_SCRATCH_BYTES (32 MiB)
+ * per GPU, created with the library's code object and held until the process
+ * ends.  The call itself allocates nothing.  Everything else (arguments,
+ * routing, outputs, results) is exactly moe_fused_forward's.
+ * Errors: as moe_fused_forward, plus MOE_ERR_CAPACITY when the layer's
+ * workspace (the size moe_fused_forward reports for these parameters) exceeds
+ * the scratch; nothing is launched then.  Every call on one GPU shares that
+ * GPU's scratch and leaves its last contents there: calls that overlap on one
+ * GPU (different streams or host threads) race and must not be issued.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int moe_fused_forward_noalloc(const moe_layer_params* p, const void* x,
+                              const float* router_logits, const void* w13, const void* w2,
+                              const void* shared_w13, const void* shared_w2, float* out,
+                              int32_t* topk_ids, float* topk_weights, int32_t* sorted_token_ids,
+                              int32_t* expert_ids, int32_t* num_tokens_post_padded,
+                              void* stream);
+
 /* Human-readable text of a status code (static storage). */
 const char* moe_status_string(int status);
 
