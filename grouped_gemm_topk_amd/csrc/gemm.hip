@@ -770,7 +770,9 @@ hipError_t launch_grouped_gemm(const GemmParams& p, int block_m, hipStream_t s) 
 
 // out[t] = sum_j yslot[t*k + j] (+ yslot[T*k + t] for the shared expert), in j order.
 __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ yslot, int T, int k,
-                                                      int H, int has_shared, float* __restrict__ out) {
+                                                      int H, int has_shared, float* __restrict__ out,
+                                                      int* __restrict__ status) {
+  if (status && blockIdx.x == 0 && threadIdx.x == 0) *status = 0;
   const int h4 = H / 4;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (int64_t)T * h4) return;
@@ -789,11 +791,11 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
 }
 
 hipError_t launch_combine(const float* yslot, int T, int k, int H, int has_shared, float* out,
-                          hipStream_t s) {
+                          int* status, hipStream_t s) {
   int64_t n = (int64_t)T * (H / 4);
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, yslot, T, k,
-                     H, has_shared, out);
+                     H, has_shared, out, status);
   return hipGetLastError();
 }
 

@@ -525,6 +525,7 @@ __global__ void __launch_bounds__(kG1Waves * 64) gemv1_kernel(GemvParams p) {
 
   const int b = blockIdx.y;
   const bool shared = b == p.nblk;
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *p.status = 0;   // no waits here
   route_prologue(p, sm.L, shared ? -1 : b, blockIdx.x == 0 && blockIdx.y == 0);
   const int e = sm.L.my_expert;
   const int r = lane & 15;   // token column of this lane (operand and result)
@@ -662,7 +663,9 @@ constexpr int kFusedMinSlots = 48;
 constexpr int kCtlStride = 32;
 // bound of the W2 workgroups' wait (polls about half a microsecond apart,
 // about a second in all): far above any W13 phase, so a stuck counter ends
-// the wait instead of the process (the output is then wrong, never hung)
+// the wait instead of the process.  The output is then wrong, and the
+// workgroup records it in the layer's status word (the word after the
+// counters, cleared by every call) for the caller to read.
 constexpr int kMaxSpin = 1 << 21;
 constexpr int kSpinSleep = 16;   // s_sleep units of 64 cycles between polls
 
@@ -677,6 +680,7 @@ __global__ void __launch_bounds__(kRouteWaves * 64) route_kernel(GemvParams p) {
     ((float4*)p.out)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
   const int nb = p.nblk + (p.sw13 ? 1 : 0);
   for (int b = threadIdx.x; b < nb; b += blockDim.x) p.ctl[b * kCtlStride] = 0;
+  if (threadIdx.x == 0) *p.status = 0;
 }
 
 // The slot of row r of block b, or -1 (a pad or no block); the shared expert's
@@ -787,6 +791,8 @@ __device__ void w2_phase(const GemvParams& p, int bx, int b, int g1x, u32x4 (*s_
                g1x &&
            ++spins < kMaxSpin)
       __builtin_amdgcn_s_sleep(kSpinSleep);
+    if (spins >= kMaxSpin)   // the wait expired: this call's output is invalid
+      __hip_atomic_store(p.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();   // the act rows are then read with device-coherent loads
   if (!active) return;

@@ -110,6 +110,7 @@ struct LayerWorkspace {
   uint16_t* act;      // [cap, I] bf16 in padded order
   uint16_t* act_sh;   // [T, I] bf16, shared expert
   int32_t* ctl;       // decode kernel's control block
+  int32_t* status;    // the layer's status word (0: every wait ended normally)
   float* logits;      // [T, E] router logits computed by the library (router path)
   float* yslot;       // [T*k (+T), H] fp32 weighted expert outputs
   size_t bytes;
@@ -130,6 +131,7 @@ LayerWorkspace layout_layer(const moe_layer_params* p, void* ws) {
   w.act_sh = (uint16_t*)c.take((size_t)(p->n_shared ? p->T : 0) * p->I * 2);
   w.yslot = (float*)c.take((size_t)(n + (p->n_shared ? p->T : 0)) * p->H * 4);
   w.ctl = (int32_t*)c.take((size_t)(moe::kMaxExperts + 1) * 32 * sizeof(int32_t));
+  w.status = (int32_t*)c.take(sizeof(int32_t));
   w.logits = (float*)c.take((size_t)p->T * p->E * sizeof(float));
   w.bytes = c.off;
   return w;
@@ -473,6 +475,7 @@ int fused_forward(const moe_layer_params* p, const void* x, const float* router_
     gv.act_sh = L.act_sh;
     gv.out = out;
     gv.ctl = L.ctl;
+    gv.status = L.status;
     if (mx) {
       gv.mx = 1;
       gv.w13_s = mx->w13;
@@ -571,7 +574,7 @@ int fused_forward(const moe_layer_params* p, const void* x, const float* router_
   if (e != hipSuccess) return hip_status(e);
 
   // ---- combine
-  e = moe::launch_combine(L.yslot, T, k, H, p->n_shared, out, s);
+  e = moe::launch_combine(L.yslot, T, k, H, p->n_shared, out, L.status, s);
   return hip_status(e);
 }
 
@@ -586,6 +589,13 @@ int moe_fused_forward(const moe_layer_params* p, const void* x, const float* rou
   return fused_forward(p, x, router_logits, false, nullptr, w13, w2, shared_w13, shared_w2, nullptr,
                        out, topk_ids, topk_weights, sorted_token_ids, expert_ids,
                        num_tokens_post_padded, workspace, workspace_bytes, stream);
+}
+
+int64_t moe_fused_forward_status_offset(const moe_layer_params* p) {
+  const int st = validate_layer(p);
+  if (st != MOE_OK) return st;
+  char* const base = (char*)nullptr + 256;   // a stand-in base, never dereferenced
+  return (int64_t)((char*)layout_layer(p, base).status - base);
 }
 
 int moe_fused_forward_noalloc(const moe_layer_params* p, const void* x,

@@ -119,6 +119,7 @@ struct GemvParams {
   uint16_t* act_sh;         // [T, I]
   float* out;               // [T, H], zeroed by GEMV1 or the route kernel, accumulated by the W2 GEMV
   int* ctl;                 // control block of the decode kernel (workspace, reset every call)
+  int* status;              // the layer's status word: 0, or 1 when a bounded wait expired
 };
 
 hipError_t launch_gemv(const GemvParams& p, bool swiglu, hipStream_t s);
@@ -148,7 +149,9 @@ hipError_t launch_seg_table(const int* expert_ids, const int* ntpp, int block_m,
 constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
 hipError_t noalloc_scratch(void** ptr);
 
+// also clears the layer's status word (`status`, may be null): the prefill
+// path has no cross-workgroup waits
 hipError_t launch_combine(const float* yslot, int T, int k, int H, int has_shared, float* out,
-                          hipStream_t s);
+                          int* status, hipStream_t s);
 
 }  // namespace moe

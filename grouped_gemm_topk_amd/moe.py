@@ -25,7 +25,7 @@ EPI_STORE, EPI_SWIGLU, EPI_RELU2, EPI_WEIGHTED_SCATTER = 0, 1, 2, 3
 
 EXPORTED = ("moe_align", "moe_grouped_gemm", "moe_grouped_gemm_backward", "moe_fused_forward",
             "moe_fused_forward_mxfp8", "moe_fused_forward_router", "moe_fused_forward_noalloc",
-            "moe_align_capacity", "moe_status_string")
+            "moe_fused_forward_status_offset", "moe_align_capacity", "moe_status_string")
 
 NOALLOC_SCRATCH_BYTES = 32 << 20
 
@@ -94,6 +94,8 @@ def lib() -> ctypes.CDLL:
         L.moe_fused_forward_noalloc.argtypes = [ctypes.POINTER(MoeLayerParams), vp, vp, vp, vp, vp,
                                                 vp, vp, vp, vp, vp, vp, vp, vp]
         L.moe_fused_forward_noalloc.restype = ctypes.c_int
+        L.moe_fused_forward_status_offset.argtypes = [ctypes.POINTER(MoeLayerParams)]
+        L.moe_fused_forward_status_offset.restype = ctypes.c_int64
         L.moe_align_capacity.argtypes = [i32, i32, i32, i32]
         L.moe_align_capacity.restype = ctypes.c_int64
         L.moe_status_string.argtypes = [ctypes.c_int]
@@ -429,10 +431,26 @@ class FusedLayer:
     def out(self) -> torch.Tensor:
         return self.tensors["out"]
 
+    def status(self) -> torch.Tensor:
+        """The layer's status word in the workspace (int32 [1] view, on the
+        device): 0 after a call whose cross-workgroup waits all ended normally,
+        1 when a bounded wait expired (that call's output is invalid)."""
+        off = int(lib().moe_fused_forward_status_offset(ctypes.byref(self._cp)))
+        if off < 0:
+            _check("moe_fused_forward_status_offset", off)
+        return self.workspace[off:off + 4].view(torch.int32)
+
     def run(self, stream=None) -> torch.Tensor:
         self._n.value = self.workspace.numel()
         _check(self._call, self._fn(*self._args, ctypes.byref(self._n), _stream(stream)))
         return self.tensors["out"]
+
+
+def _with_status(layer: "FusedLayer") -> dict:
+    r = dict(layer.routing)
+    if layer.p.T > 0:
+        r["status"] = layer.status()
+    return r
 
 
 def moe_fused_forward_mxfp8(p: LayerParams, x, router_logits, w13_q, w13_scale, w2_q, w2_scale,
@@ -440,7 +458,8 @@ def moe_fused_forward_mxfp8(p: LayerParams, x, router_logits, w13_q, w13_scale, 
                             shared_w2_scale=None, out=None, return_routing: bool = False,
                             stream=None):
     """The layer with MXFP8 expert weights (decode shapes, T <= 16): uint8 FP8
-    E4M3 weight bytes and uint8 E8M0 scales, one per 32 elements along a row."""
+    E4M3 weight bytes and uint8 E8M0 scales, one per 32 elements along a row.
+    With ``return_routing`` the dict also holds ``status`` (see FusedLayer.status)."""
     sc = {"w13": w13_scale, "w2": w2_scale}
     if p.n_shared:
         sc["shared_w13"], sc["shared_w2"] = shared_w13_scale, shared_w2_scale
@@ -448,7 +467,7 @@ def moe_fused_forward_mxfp8(p: LayerParams, x, router_logits, w13_q, w13_scale, 
                        routing_outputs=return_routing, scales=sc)
     if p.T > 0:
         layer.run(stream)
-    return (layer.out, layer.routing) if return_routing else layer.out
+    return (layer.out, _with_status(layer)) if return_routing else layer.out
 
 
 def moe_fused_forward_router(p: LayerParams, x, router_w, w13, w2, shared_w13=None,
@@ -460,19 +479,20 @@ def moe_fused_forward_router(p: LayerParams, x, router_w, w13, w2, shared_w13=No
     if p.T > 0:
         layer.run(stream)
     if return_routing:
-        return layer.out, {**layer.routing, "router_logits": layer.tensors["logits"]}
+        return layer.out, {**_with_status(layer), "router_logits": layer.tensors["logits"]}
     return layer.out
 
 
 def moe_fused_forward(p: LayerParams, x, router_logits, w13, w2, shared_w13=None, shared_w2=None,
                       out=None, return_routing: bool = False, stream=None):
     """The whole MoE layer.  Returns ``out`` (fp32 [T,H]) or, with
-    ``return_routing``, ``(out, routing_dict)``."""
+    ``return_routing``, ``(out, routing_dict)``; the dict also holds the
+    call's ``status`` word (see FusedLayer.status)."""
     layer = FusedLayer(p, x, router_logits, w13, w2, shared_w13, shared_w2, out,
                        routing_outputs=return_routing)
     if p.T > 0:
         layer.run(stream)
-    return (layer.out, layer.routing) if return_routing else layer.out
+    return (layer.out, _with_status(layer)) if return_routing else layer.out
 
 
 def moe_fused_forward_noalloc(p: LayerParams, x, router_logits, w13, w2, shared_w13=None,

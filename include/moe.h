@@ -286,6 +286,20 @@ int moe_fused_forward_mxfp8(const moe_layer_params* p, const void* x, const floa
                             size_t* workspace_bytes, void* stream);
 
 /*
+ * Byte offset, inside the workspace of moe_fused_forward (and its _router and
+ * _mxfp8 forms) for these parameters, of the layer's int32 status word, or a
+ * negative status for invalid parameters.  Every call with T > 0 rewrites the
+ * word on its stream: 0 when every cross-workgroup wait of the call ended
+ * normally, 1 when a bounded wait expired, in which case that call's output
+ * is invalid.  Only the decode form with one launch for both expert GEMVs
+ * (T <= 16 and T * top_k >= 48) waits across workgroups: its W2 workgroups
+ * wait, bounded at about a second, for the W13 workgroups of their expert,
+ * relying on workgroups being dispatched in index order.  Read the word after
+ * the call has completed (the library itself never reads it back).
+ */
+int64_t moe_fused_forward_status_offset(const moe_layer_params* p);
+
+/*
  * moe_fused_forward without a workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid allocation).  The library's own device-resident

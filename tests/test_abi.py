@@ -253,3 +253,16 @@ def test_fused_forward_router_validation(L):
     args = [fake] * 14
     args[1] = fake + 4   # router_w misaligned
     assert L.moe_fused_forward_router(ctypes.byref(p), *args, ctypes.byref(ok), None) == -5
+
+
+def test_status_offset(L):
+    """The status word lies inside the layer's workspace, 4-byte aligned, for
+    prefill and decode shapes; invalid parameters give their status."""
+    for kw in (dict(), dict(T=1, E=128, top_k=8), dict(T=4096, H=3072, I=2560, E=18, top_k=4,
+                                                       block_m=128, n_shared=1)):
+        p = _layer(**kw).c_struct()
+        n = ctypes.c_size_t(0)
+        assert L.moe_fused_forward(ctypes.byref(p), *([None] * 13), ctypes.byref(n), None) == 0
+        off = L.moe_fused_forward_status_offset(ctypes.byref(p))
+        assert 0 <= off and off + 4 <= n.value and off % 4 == 0
+    assert L.moe_fused_forward_status_offset(ctypes.byref(_layer(block_m=24).c_struct())) == -2

@@ -45,6 +45,7 @@ def _run(moe, cfg, inp, mx, routing=True):
 
 
 def _check(cfg, inp, mx, got, r):
+    assert int(r["status"].item()) == 0, "status word set"
     ref = O.moe_forward_mxfp8_cfg(cfg, inp, mx)
     assert np.array_equal(r["topk_ids"].cpu().numpy(), ref["topk_ids"])
     nt = int(r["num_tokens_post_padded"].cpu().item())

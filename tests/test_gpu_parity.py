@@ -27,6 +27,8 @@ def moe():
 
 
 def _check_routing(res_gpu, ref, T, k, bm):
+    if "status" in res_gpu:   # every bounded cross-workgroup wait ended normally
+        assert int(res_gpu["status"].item()) == 0, "status word set"
     ids = res_gpu["topk_ids"].cpu().numpy()
     assert np.array_equal(ids, ref["topk_ids"]), "topk_ids"
     np.testing.assert_allclose(res_gpu["topk_weights"].cpu().numpy(), ref["topk_weights"],

@@ -44,6 +44,7 @@ def _check_logits(inp, wr, got):
 
 
 def _check_routing(cfg, r):
+    assert int(r["status"][0]) == 0, "status word set"
     ids, wts = O.gate(r["router_logits"], cfg.top_k, cfg.scoring, cfg.n_group, cfg.topk_group,
                       cfg.renormalize, cfg.scale)
     assert np.array_equal(r["topk_ids"], ids)

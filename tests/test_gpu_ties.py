@@ -17,7 +17,6 @@ the C ABI by the shape that selects it:
 topk_ids, sorted_token_ids, expert_ids and num_tokens_post_padded must be bit
 for bit the oracle's; weights and the layer output are held to the usual bars.
 """
-import dataclasses
 
 import numpy as np
 import pytest
@@ -39,6 +38,7 @@ def moe():
 
 
 def _check_routing(r, ids, wts, E, bm):
+    assert int(r["status"].item()) == 0, "status word set"
     got_ids = r["topk_ids"].cpu().numpy()
     assert np.array_equal(got_ids, ids), f"topk_ids\n{got_ids}\n{ids}"
     np.testing.assert_allclose(r["topk_weights"].cpu().numpy(), wts, rtol=2e-6, atol=1e-7)
