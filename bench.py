@@ -49,10 +49,10 @@ PREFILL_CASES = ("zipf128", "relu2_t2048")
 # digest; any other source reports traffic null until it is measured again.
 DOMINANT_TRAFFIC = {
     "src": "grouped_gemm_topk_amd/csrc/gemm.hip",
-    "sha256": "f3cf547573cf7b2a97d86d1a33e96e430c6eff36a79dfa04a6dbdf1ade23c868",
+    "sha256": "244951346133218d11554e82334d2e46233afd7563a2cb7f8d7666dbd92035eb",
     "config": "dsv3",
-    "fetch_bytes": 1320452160,
-    "write_bytes": 89789088,
+    "fetch_bytes": 1268214374,
+    "write_bytes": 89790362,
 }
 
 
