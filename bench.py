@@ -49,10 +49,10 @@ PREFILL_CASES = ("zipf128", "relu2_t2048")
 # digest; any other source reports traffic null until it is measured again.
 DOMINANT_TRAFFIC = {
     "src": "grouped_gemm_topk_amd/csrc/gemm.hip",
-    "sha256": "244951346133218d11554e82334d2e46233afd7563a2cb7f8d7666dbd92035eb",
+    "sha256": "8222d64f696e846306392f25538a3cdb02289180f13e458d1fd15a1a797b009a",
     "config": "dsv3",
-    "fetch_bytes": 1268214374,
-    "write_bytes": 89790362,
+    "fetch_bytes": 1284615637,
+    "write_bytes": 89787904,
 }
 
 
