@@ -49,10 +49,10 @@ PREFILL_CASES = ("zipf128", "relu2_t2048")
 # digest; any other source reports traffic null until it is measured again.
 DOMINANT_TRAFFIC = {
     "src": "grouped_gemm_topk_amd/csrc/gemm.hip",
-    "sha256": "8222d64f696e846306392f25538a3cdb02289180f13e458d1fd15a1a797b009a",
+    "sha256": "fa1da8ccf8879d2719b99ff2fc3b5d337a561339da519df127feb9f9cd525092",
     "config": "dsv3",
-    "fetch_bytes": 1284615637,
-    "write_bytes": 89787904,
+    "fetch_bytes": 898857920,
+    "write_bytes": 94400251,
 }
 
 

@@ -27,14 +27,19 @@
 // range, the tiles of one expert's run of M-blocks are consecutive, in chunks
 // of 8 M-blocks per N-tile, so that a weight tile and the token rows are
 // reused from that XCD's L2 (the L2 grouping / cache-aware scheduling of the
-// skill card's *Optimization Patterns*).  With the 128-row tile the grid is
-// one workgroup per CU and each workgroup runs a sequence of tiles: between
-// two tiles it requests the next tile's first K steps and then writes the
-// finished tile while they are in flight, and the global reads a tile's
-// set-up needs (sorted token ids, routed weights) are issued a tile ahead;
-// the expert ids of the m-blocks sit in LDS for the tile mapping.
-// v_mfma_f32_32x32x16_bf16 is used when a wave owns >= 32 token rows,
-// v_mfma_f32_16x16x32_bf16 for BLOCK_M = 16.
+// skill card's *Optimization Patterns*).  With the 128- and 256-row tiles
+// the grid is one workgroup per CU and each workgroup runs a sequence of
+// tiles; the expert ids of the m-blocks sit in LDS for the tile mapping.  The
+// 128-row tile (three LDS stages) splits its waves: eight compute waves
+// multiply out of LDS and write the tiles, eight loader waves issue every
+// direct load, two K steps ahead, in one sequence across the tile boundaries,
+// so the compute waves' stores never wait in a load counter.  The 256-row
+// tile (two stages, no room for loader waves' registers) has every wave load
+// and compute: between two tiles it requests the next tile's first K step
+// and then writes the finished tile while it is in flight, and the global
+// reads a tile's set-up needs (sorted token ids, routed weights) are issued a
+// tile ahead.  v_mfma_f32_32x32x16_bf16 is used when a wave owns >= 32 token
+// rows, v_mfma_f32_16x16x32_bf16 for BLOCK_M = 16.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -104,6 +109,12 @@ __device__ __forceinline__ int swz(int r, int c) {
 #ifndef MOE_GM
 #define MOE_GM 8   // m-blocks per tile chunk
 #endif
+#ifndef MOE_PC
+#define MOE_PC 1   // loader / compute split for persistent 128-row tiles
+#endif
+#ifndef MOE_NLW
+#define MOE_NLW 8   // loader waves of the split
+#endif
 
 __device__ __forceinline__ int xcd_tile(int L, int n) {
   // workgroups are handed to the 8 XCDs round-robin by linear id: give XCD x
@@ -140,7 +151,7 @@ __device__ __forceinline__ void expert_run(Id id, int mb0, int vb, int lane, int
 // expert ids kept in LDS by the 128-row tile (its three stages leave 16 KB of
 // the 160 KB; the smaller tiles run two workgroups per CU and keep none)
 template <int BM>
-constexpr int kEidsLds = BM == 128 ? 2048 : 0;
+constexpr int kEidsLds = BM >= 128 ? 2048 : 0;
 
 // BM token rows x BNW weight rows per workgroup tile, WAVES_M x WAVES_N waves,
 // BK-wide K steps, NS LDS stages (direct path: loads for step kt + NS - 1 are
@@ -148,9 +159,15 @@ constexpr int kEidsLds = BM == 128 ? 2048 : 0;
 // SW: the tile's first BNW/2 weight rows are gate rows n0.., the rest the up
 // rows I+n0.. of the same act columns, and the epilogue is SwiGLU.
 // WNT: weight rows are loaded with the non-temporal hint (see launch_bm).
-template <int BM, int BNW, int WAVES_M, int WAVES_N, bool SW, int BK, int NS, int MINW, bool WNT = false>
-__global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) grouped_gemm_kernel(GemmParams pin) {
-  constexpr int NT = 64 * WAVES_M * WAVES_N;   // threads of the workgroup
+// PC: MOE_NLW more waves (loader waves) issue every direct load and the
+// WAVES_M x WAVES_N waves only compute and store (see the PC branch below).
+template <int BM, int BNW, int WAVES_M, int WAVES_N, bool SW, int BK, int NS, int MINW,
+          bool WNT = false, bool PC = false>
+__global__ void __launch_bounds__(64 * (WAVES_M * WAVES_N + (PC ? MOE_NLW : 0)), MINW)
+    grouped_gemm_kernel(GemmParams pin) {
+  constexpr int NCW = WAVES_M * WAVES_N;        // compute waves
+  constexpr int NT = 64 * (NCW + (PC ? MOE_NLW : 0));   // threads of the workgroup
+  constexpr int LT = PC ? 64 * MOE_NLW : NT;            // threads that issue direct loads
   constexpr int CPR = BK / 8;
   constexpr int WM = BM / WAVES_M;
   constexpr int MT = WM >= 32 ? 32 : 16;
@@ -159,11 +176,11 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) grouped_gemm_ker
   constexpr int WNW = BNW / WAVES_N;
   constexpr int FM = WM / MT;
   constexpr int FN = WNW / MT;
-  constexpr int XL = (BM * CPR + NT - 1) / NT;
-  constexpr int WL = BNW * CPR / NT;
-  static_assert(WAVES_M * WAVES_N >= 4 && WAVES_M * WAVES_N <= 8, "4 to 8 waves");
+  constexpr int XL = (BM * CPR + LT - 1) / LT;
+  constexpr int WL = BNW * CPR / LT;
+  static_assert(NCW >= 4 && NCW <= 8, "4 to 8 compute waves");
   static_assert(!SW || FN % 2 == 0, "SwiGLU pairs gate and up subtiles");
-  static_assert(BNW * CPR % NT == 0, "weight tile load");
+  static_assert(BNW * CPR % LT == 0, "weight tile load");
   static_assert(KSTEPS >= 1, "K step");
 
   // LDS stages (loads run NS - 1 K steps ahead)
@@ -177,6 +194,9 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) grouped_gemm_ker
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
   const int wn = wave % WAVES_N;
   const int wm = wave / WAVES_N;
+  // the loader threads: all of them, or the loader waves after the compute waves
+  const int ltid = PC ? tid - 64 * NCW : tid;
+  const int lwave = PC ? wave - NCW : wave;
 
   // ---- the tiles of this launch.  Tiles are numbered XCD by XCD: tile L of
   // the launch's sequence goes to XCD L mod 8 (the order in which workgroups
@@ -329,7 +349,7 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) grouped_gemm_ker
   auto load_ids = [&](const Tile& t, int* xs, int* es) {
 #pragma unroll
     for (int q = 0; q < XL; ++q) {
-      const int u = tid + NT * q;
+      const int u = ltid + LT * q;
       const int i = t.m0 + u / CPR;
       xs[q] = (u < BM * CPR && t.sorted) ? t.sorted[i] : i;
     }
@@ -347,7 +367,7 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) grouped_gemm_ker
   auto offsets = [&](const Tile& t, const int* xs, int* xdo, int* wdo) {
 #pragma unroll
     for (int q = 0; q < XL; ++q) {
-      const int u = tid + NT * q;
+      const int u = ltid + LT * q;
       const int r = u / CPR;
       const int c = (u % CPR) ^ ((r / (16 / CPR)) % CPR);
       xdo[q] = kNoRow;
@@ -365,7 +385,7 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) grouped_gemm_ker
     }
 #pragma unroll
     for (int q = 0; q < WL; ++q) {
-      const int u = tid + NT * q;
+      const int u = ltid + LT * q;
       const int r = u / CPR;
       const int c = (u % CPR) ^ ((r / (16 / CPR)) % CPR);
       int g;
@@ -487,25 +507,15 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) grouped_gemm_ker
   // vmcnt(n) with the other counters left alone
 #define MOE_VMW(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
 
-  // the first tile, set up in full
-  int L = blockIdx.x;
-  Tile cur = tile_of(resolve(L));
-  int xs[XL], es[FM];
-  load_ids(cur, xs, es);
-  MOE_VMW(0);
+  // the loader thread's direct-load offsets and buffer descriptors for the
+  // tile it is loading
   int xdo[XL], wdo[WL];
-  EpiRows er;
-  float sc[FM];
-  offsets(cur, xs, xdo, wdo);
-  epi_rows(cur, es, er);
-  load_scale(cur, er, sc);
-  i32x4 xr4 = rsrc4(cur.A, cur.a_bytes);
-  i32x4 wr4 = rsrc4(cur.W, cur.w_bytes);
-  int K = cur.K;
+  i32x4 xr4, wr4;
+  int K = pin.K;
 
   // this wave issues the last of the XL token-row loads (waves past the end of
   // the token tile skip it)
-  const bool x_wave = NT * (XL - 1) + 64 * wave < BM * CPR;
+  const bool x_wave = LT * (XL - 1) + 64 * lwave < BM * CPR;
   // load i (of XL + WL per thread) of K step kt into LDS buffer b: the first
   // XL are token-row chunks, the rest weight-row chunks; the ragged last K
   // step (tail) masks the 16-byte chunks beyond K
@@ -514,17 +524,18 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) grouped_gemm_ker
     const int k0 = kt * BK;
     const bool is_x = i < XL;
     const int q = is_x ? i : i - XL;
-    if (is_x && NT * q + 64 * wave >= BM * CPR) return;   // wave-uniform
-    const int u = tid + NT * q;
+    if (is_x && LT * q + 64 * lwave >= BM * CPR) return;   // wave-uniform
+    const int u = ltid + LT * q;
     int off = is_x ? xdo[is_x ? q : 0] : wdo[is_x ? 0 : q], soff = k0 * 2;
     if constexpr (tail) {
       const int c = (u % CPR) ^ ((u / CPR / (16 / CPR)) % CPR);
       off = (k0 + c * 8 < K && off != kNoRow) ? off + k0 * 2 : kNoRow;
       soff = 0;
     }
-    if (is_x) dma1(xr4, lds_x + (unsigned)((b * BM * CPR + NT * q + 64 * wave) * 16), off, soff);
-    else if constexpr (WNT) dma1_nt(wr4, lds_w + (unsigned)((b * BNW * CPR + NT * q + 64 * wave) * 16), off, soff);
-    else dma1(wr4, lds_w + (unsigned)((b * BNW * CPR + NT * q + 64 * wave) * 16), off, soff);
+    const unsigned unit = (unsigned)(LT * q + 64 * lwave);
+    if (is_x) dma1(xr4, lds_x + (unsigned)((b * BM * CPR + unit) * 16), off, soff);
+    else if constexpr (WNT) dma1_nt(wr4, lds_w + (unsigned)((b * BNW * CPR + unit) * 16), off, soff);
+    else dma1(wr4, lds_w + (unsigned)((b * BNW * CPR + unit) * 16), off, soff);
   };
   // the direct loads [i0, i1) of K step kt into LDS buffer b (all of them:
   // [0, XL + WL); the weight chunks alone: [XL, XL + WL))
@@ -549,7 +560,9 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) grouped_gemm_ker
   };
   // the MFMAs of substep kk with this thread's loads of a later K step spread
   // between them: load i follows MFMA i * TM / ND of the step, so the address
-  // queue drains while the matrix cores work
+  // queue drains while the matrix cores work (the 256-row tile, one step
+  // ahead only, issues them within the first quarter of the step's MFMAs:
+  // 2-4 % faster than across the whole step)
   auto mfmas_spread = [&](const Ops& o, int kk, auto&& load_i) {
     constexpr int TM = KSTEPS * FN * FM;
     constexpr int ND = XL + WL;
@@ -561,7 +574,7 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) grouped_gemm_ker
         const int m = (kk * FN + f) * FM + q;
 #pragma unroll
         for (int i = 0; i < ND; ++i)
-          if (i * TM / ND == m) load_i(i);
+          if (i * TM / (BM == 256 ? 4 * ND : ND) == m) load_i(i);
       }
   };
 
@@ -574,7 +587,7 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) grouped_gemm_ker
   // tile's first D steps go to the D buffers the last step did not read.
   constexpr int NXW = XL + WL;
   constexpr int NW = WL + XL - 1;
-  static_assert((BM * CPR - NT * (XL - 1)) % 64 == 0, "the last token-row load is whole waves");
+  static_assert((BM * CPR - LT * (XL - 1)) % 64 == 0, "the last token-row load is whole waves");
   constexpr int D = NBUF - 1;   // prefetch distance in K steps
   static_assert((D - 1) * NXW <= 63, "vmcnt range");
   // wait until this thread's loads of the oldest pending step have landed;
@@ -593,82 +606,9 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) grouped_gemm_ker
       if (st < nk) dma_part(st, (b + st) % NBUF, 0, XL);
   };
 
-  int b0 = 0;
-  first_steps(0, (K + BK - 1) / BK);
-  // the second tile: mapping and row ids
-  int Ln = L + G;
-  Tile nxt = cur;
-  if (Ln < nvalid) {
-    nxt = tile_of(resolve(Ln));
-    load_ids(nxt, xs, es);
-  }
-  wait_all();
-  __builtin_amdgcn_s_barrier();
-  for (;;) {
-    const int nk = (K + BK - 1) / BK;
-#pragma unroll
-    for (int f = 0; f < FN; ++f)
-#pragma unroll
-      for (int q = 0; q < FM; ++q)
-#pragma unroll
-        for (int v = 0; v < M::kVals; ++v) acc[f][q][v] = 0.f;
-    for (int kt = 0; kt < nk; ++kt) {
-      const int bd = b0 == 0 ? NBUF - 1 : b0 - 1;   // the buffer of step kt + D
-      // 0: no load this step, 1: a full K step, 2: the ragged last K step
-      const int dmode = kt + D < nk ? ((kt + D + 1) * BK > K ? 2 : 1) : 0;
-      auto load_i = [&](int i) {
-        if (dmode == 1) dma_one(std::false_type{}, kt + D, bd, i);
-        else if (dmode == 2) dma_one(std::true_type{}, kt + D, bd, i);
-      };
-      const u32x4* const rx = sX[b0];
-      const u32x4* const rw = sW[b0];
-      Ops sa, sb;
-      read_ops(rx, rw, 0, sa);
-#pragma unroll
-      for (int kk = 0; kk < KSTEPS; kk += 2) {
-        if (kk + 1 < KSTEPS) read_ops(rx, rw, kk + 1, sb);
-        mfmas_spread(sa, kk, load_i);
-        if (kk + 2 < KSTEPS) read_ops(rx, rw, kk + 2, sa);
-        if (kk + 1 < KSTEPS) mfmas_spread(sb, kk + 1, load_i);
-      }
-      if (kt + 1 < nk) {
-        // this thread's part of step kt + 1 has landed; steps kt + 2 .. kt + D
-        // (those issued) may still be in flight
-        if (kt + D <= nk - 1) wait_steady(); else wait_all();
-        __builtin_amdgcn_s_barrier();
-      }
-      b0 = b0 == NBUF - 1 ? 0 : b0 + 1;
-    }
-
-    // ---- between tiles (the same K: segmented launches run one tile per
-    // workgroup).  No direct load is in flight here, so waiting for the reads
-    // issued a tile ago costs nothing.
-    MOE_VMW(0);
-    const Tile done = cur;
-    const EpiRows der = er;
-    float dsc[FM];
-#pragma unroll
-    for (int q = 0; q < FM; ++q) dsc[q] = sc[q];
-    const bool more = Ln < nvalid;
-    if (more) {
-      // the next tile: its first D steps, then its routed weights
-      cur = nxt;
-      offsets(cur, xs, xdo, wdo);
-      epi_rows(cur, es, er);
-      xr4 = rsrc4(cur.A, cur.a_bytes);
-      wr4 = rsrc4(cur.W, cur.w_bytes);
-      K = cur.K;
-      first_steps(b0, (K + BK - 1) / BK);
-      load_scale(cur, er, sc);
-      // the tile after it: mapping and row ids
-      Ln += G;
-      if (Ln < nvalid) {
-        nxt = tile_of(resolve(Ln));
-        load_ids(nxt, xs, es);
-      }
-    }
-
-    // ---- epilogue of the finished tile
+  // the epilogue of a finished tile: activation or routed-weight scale, then
+  // the stores of this lane's outputs
+  auto epilogue = [&](const Tile& done, const EpiRows& der, const float* dsc) {
 #pragma unroll
     for (int q = 0; q < FM; ++q) {
       if (!der.ok[q]) continue;
@@ -709,10 +649,257 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) grouped_gemm_ker
         }
       }
     }
-    if (!more) break;
-    // the next tile's first steps (and this tile's stores) have landed
+  };
+  auto zero_acc = [&]() {
+#pragma unroll
+    for (int f = 0; f < FN; ++f)
+#pragma unroll
+      for (int q = 0; q < FM; ++q)
+#pragma unroll
+        for (int v = 0; v < M::kVals; ++v) acc[f][q][v] = 0.f;
+  };
+
+  if constexpr (PC) {
+    // ---- loader / compute split.  Every tile of the launch has the same K,
+    // so the workgroup's work is C = (its tiles) x nk K steps in one sequence,
+    // and cycle c ends with barrier c.  In cycle c the compute waves multiply
+    // step c out of LDS buffer c mod 3; the loader waves issue all loads of
+    // step c + 2 at once into the buffer step c - 1 used (every compute wave
+    // is past barrier c - 1, so done reading it), wait until their loads of
+    // step c + 1 have landed and meet the compute waves at barrier c.  The
+    // sequence runs on across tile boundaries: the loads of the next tile's
+    // first steps are in flight while the compute waves finish a tile and
+    // write it.  The compute waves issue no direct loads and wait for no
+    // load counter in the K loop, so their stores never hold up the pipeline;
+    // the loader waves' counter holds their direct loads only, so the waits
+    // are compile-time counts.
+    static_assert(D == 2 && XL * LT == BM * CPR, "loader split: three stages, whole loads");
+    constexpr int NL = XL + WL;   // direct loads per loader thread and K step
+    // the sorted token ids of tile j, which the loader threads need for their
+    // row offsets, are read by the compute waves with ordinary loads and put
+    // in s_ids[j mod R] during the epilogue of tile j - J, and read by the
+    // loader waves in cycle j * nk - 2; J keeps that at least one barrier
+    // after the write, and R >= J keeps a buffer from being rewritten before
+    // it was read
+    constexpr int R = 4;
+    __shared__ int s_ids[R][BM];
+    const int L0 = blockIdx.x;
+    const int ntl = (nvalid - L0 + G - 1) / G;   // tiles of this workgroup (>= 1)
+    const int nk = (K + BK - 1) / BK;
+    const int C = ntl * nk;
+    const int J = nk >= 3 ? 2 : (nk == 2 ? 3 : 4);   // (J - 1) * nk >= 3, J <= R
+    auto tile_at = [&](int i) { return tile_of(resolve(L0 + i * G)); };
+    // a barrier the compiler moves no memory access across; the compute
+    // waves' LDS writes (the ids) have completed before they reach it
+    auto bar = [] {
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    };
+    auto bar_c = [&] {
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0), the other counters left alone
+      bar();
+    };
+
+    if (wave >= NCW) {
+      // ---- loader waves
+      auto setup = [&](int i) {
+        const Tile t = tile_at(i);
+        int xs[XL];
+#pragma unroll
+        for (int q = 0; q < XL; ++q) xs[q] = t.sorted ? s_ids[i % R][(ltid + LT * q) / CPR] : 0;
+        offsets(t, xs, xdo, wdo);
+        xr4 = rsrc4(t.A, t.a_bytes);
+        wr4 = rsrc4(t.W, t.w_bytes);
+      };
+      // (the descriptors are wave-uniform, but carried around the loop the
+      // compiler no longer knows it: made uniform again before each step)
+      auto unif = [](i32x4& v) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) v[w] = __builtin_amdgcn_readfirstlane(v[w]);
+      };
+      auto issue = [&](int st) {   // all loads of step st of the sequence
+        const int i = st / nk, kt = st - i * nk;
+        if (kt == 0) setup(i);
+        unif(xr4);
+        unif(wr4);
+        dma_part(kt, st % NBUF, 0, NL);
+      };
+      bar();   // the first tiles' ids are in LDS
+      const int np = C < 2 ? C : 2;
+      for (int st = 0; st < np; ++st) issue(st);
+      if (np == 2) MOE_VMW(NL); else MOE_VMW(0);
+      bar();
+      for (int c = 0; c < C; ++c) {
+        if (c + 2 < C) {
+          issue(c + 2);
+          MOE_VMW(NL);   // step c + 1 has landed; step c + 2 may be in flight
+        } else if (c + 1 < C) {
+          MOE_VMW(0);
+        }
+        bar();
+      }
+    } else {
+      // ---- compute waves
+      auto load_es = [&](const Tile& t, int* es) {
+#pragma unroll
+        for (int q = 0; q < FM; ++q) {
+          const int i = t.m0 + wm * WM + q * MT + M::out_col(lane);
+          es[q] = t.sorted ? t.sorted[i] : i;
+        }
+      };
+      auto load_ids_of = [&](int j) -> int {   // thread tid < BM: tile j's row tid
+        const Tile t = tile_at(j);
+        return (tid < BM && t.sorted) ? t.sorted[t.m0 + tid] : 0;
+      };
+      Tile tc = tile_at(0), tn = tc;
+      int es[FM];
+      EpiRows er;
+      float sc[FM];
+      load_es(tc, es);
+      epi_rows(tc, es, er);
+      load_scale(tc, er, sc);
+      if (ntl > 1) {
+        tn = tile_at(1);
+        load_es(tn, es);
+      }
+      for (int j = 0; j < J && j < ntl; ++j) {
+        const int v = load_ids_of(j);
+        if (tid < BM) s_ids[j % R][tid] = v;
+      }
+      int pid = J < ntl ? load_ids_of(J) : 0;
+      bar_c();   // the first tiles' ids are in LDS
+      bar();     // the first step has landed
+      auto noload = [](int) {};
+      int b0 = 0;
+      for (int i = 0; i < ntl; ++i) {
+        zero_acc();
+        for (int kt = 0; kt < nk; ++kt) {
+          const u32x4* const rx = sX[b0];
+          const u32x4* const rw = sW[b0];
+          Ops sa, sb;
+          read_ops(rx, rw, 0, sa);
+#pragma unroll
+          for (int kk = 0; kk < KSTEPS; kk += 2) {
+            if (kk + 1 < KSTEPS) read_ops(rx, rw, kk + 1, sb);
+            mfmas_spread(sa, kk, noload);
+            if (kk + 2 < KSTEPS) read_ops(rx, rw, kk + 2, sa);
+            if (kk + 1 < KSTEPS) mfmas_spread(sb, kk + 1, noload);
+          }
+          bar_c();
+          b0 = b0 == NBUF - 1 ? 0 : b0 + 1;
+        }
+        epilogue(tc, er, sc);
+        if (i + 1 < ntl) {
+          // tile i + 1's epilogue rows and routed weights, tile i + 2's rows,
+          // and the sorted ids the loader waves need J tiles ahead
+          tc = tn;
+          epi_rows(tc, es, er);
+          load_scale(tc, er, sc);
+          if (i + 2 < ntl) {
+            tn = tile_at(i + 2);
+            load_es(tn, es);
+          }
+          if (i + J < ntl) {
+            if (tid < BM) s_ids[(i + J) % R][tid] = pid;
+            if (i + J + 1 < ntl) pid = load_ids_of(i + J + 1);
+          }
+        }
+      }
+    }
+  } else {
+    // the first tile, set up in full
+    int L = blockIdx.x;
+    Tile cur = tile_of(resolve(L));
+    int xs[XL], es[FM];
+    load_ids(cur, xs, es);
+    MOE_VMW(0);
+    EpiRows er;
+    float sc[FM];
+    offsets(cur, xs, xdo, wdo);
+    epi_rows(cur, es, er);
+    load_scale(cur, er, sc);
+    xr4 = rsrc4(cur.A, cur.a_bytes);
+    wr4 = rsrc4(cur.W, cur.w_bytes);
+    K = cur.K;
+
+    int b0 = 0;
+    first_steps(0, (K + BK - 1) / BK);
+    // the second tile: mapping and row ids
+    int Ln = L + G;
+    Tile nxt = cur;
+    if (Ln < nvalid) {
+      nxt = tile_of(resolve(Ln));
+      load_ids(nxt, xs, es);
+    }
     wait_all();
     __builtin_amdgcn_s_barrier();
+    for (;;) {
+      const int nk = (K + BK - 1) / BK;
+      zero_acc();
+      for (int kt = 0; kt < nk; ++kt) {
+        const int bd = b0 == 0 ? NBUF - 1 : b0 - 1;   // the buffer of step kt + D
+        // 0: no load this step, 1: a full K step, 2: the ragged last K step
+        const int dmode = kt + D < nk ? ((kt + D + 1) * BK > K ? 2 : 1) : 0;
+        auto load_i = [&](int i) {
+          if (dmode == 1) dma_one(std::false_type{}, kt + D, bd, i);
+          else if (dmode == 2) dma_one(std::true_type{}, kt + D, bd, i);
+        };
+        const u32x4* const rx = sX[b0];
+        const u32x4* const rw = sW[b0];
+        Ops sa, sb;
+        read_ops(rx, rw, 0, sa);
+  #pragma unroll
+        for (int kk = 0; kk < KSTEPS; kk += 2) {
+          if (kk + 1 < KSTEPS) read_ops(rx, rw, kk + 1, sb);
+          mfmas_spread(sa, kk, load_i);
+          if (kk + 2 < KSTEPS) read_ops(rx, rw, kk + 2, sa);
+          if (kk + 1 < KSTEPS) mfmas_spread(sb, kk + 1, load_i);
+        }
+        if (kt + 1 < nk) {
+          // this thread's part of step kt + 1 has landed; steps kt + 2 .. kt + D
+          // (those issued) may still be in flight
+          if (kt + D <= nk - 1) wait_steady(); else wait_all();
+          __builtin_amdgcn_s_barrier();
+        }
+        b0 = b0 == NBUF - 1 ? 0 : b0 + 1;
+      }
+
+      // ---- between tiles (the same K: segmented launches run one tile per
+      // workgroup).  No direct load is in flight here, so waiting for the reads
+      // issued a tile ago costs nothing.
+      MOE_VMW(0);
+      const Tile done = cur;
+      const EpiRows der = er;
+      float dsc[FM];
+  #pragma unroll
+      for (int q = 0; q < FM; ++q) dsc[q] = sc[q];
+      const bool more = Ln < nvalid;
+      if (more) {
+        // the next tile: its first D steps, then its routed weights
+        cur = nxt;
+        offsets(cur, xs, xdo, wdo);
+        epi_rows(cur, es, er);
+        xr4 = rsrc4(cur.A, cur.a_bytes);
+        wr4 = rsrc4(cur.W, cur.w_bytes);
+        K = cur.K;
+        first_steps(b0, (K + BK - 1) / BK);
+        load_scale(cur, er, sc);
+        // the tile after it: mapping and row ids
+        Ln += G;
+        if (Ln < nvalid) {
+          nxt = tile_of(resolve(Ln));
+          load_ids(nxt, xs, es);
+        }
+      }
+
+      // ---- epilogue of the finished tile
+      epilogue(done, der, dsc);
+      if (!more) break;
+      // the next tile's first steps (and this tile's stores) have landed
+      wait_all();
+      __builtin_amdgcn_s_barrier();
+    }
   }
 #undef MOE_VMW
 }
@@ -743,10 +930,10 @@ hipError_t launch_bm(GemmParams p, hipStream_t s) {
   if (p.nseg > 0) p.nsb = 0;
   int64_t nwg = (int64_t)(p.mblocks + p.nsb) * p.ntiles_n * (p.nseg > 0 ? p.nseg : 1);
   if (nwg == 0) return hipSuccess;
-  // one workgroup per CU (the LDS of the 128-row tile admits no second one),
+  // one workgroup per CU (the LDS of the 128- and 256-row tiles admits no second one),
   // each running tiles gridDim.x apart; the CU count is a multiple of 8, so a
   // workgroup stays on the XCD its tiles are numbered for
-  if (BM == 128 && p.nseg == 0) {
+  if (BM >= 128 && p.nseg == 0) {
     const int ncu = cu_count();
     if (ncu > 0 && ncu % 8 == 0 && nwg > ncu) nwg = ncu;
   }
@@ -759,6 +946,25 @@ hipError_t launch_bm(GemmParams p, hipStream_t s) {
   const bool wnt = BM == 128 && p.nseg == 0 && p.M2 == 0 && p.expert_ids &&
                    (int64_t)p.num_valid <= (int64_t)p.E * BM;
   const dim3 grid((unsigned)nwg), block(64 * WAVES_M * WAVES_N);
+  if constexpr (BM == 128 && NS == 3) {
+    // persistent 128-row tiles with one K: the loader / compute split
+    if (p.nseg == 0 && MOE_PC) {
+      const dim3 block_pc(64 * (WAVES_M * WAVES_N + MOE_NLW));
+      if (wnt && sw)
+        hipLaunchKernelGGL((grouped_gemm_kernel<BM, BNW, WAVES_M, WAVES_N, true, BK, NS, MINW, true, true>),
+                           grid, block_pc, 0, s, p);
+      else if (wnt)
+        hipLaunchKernelGGL((grouped_gemm_kernel<BM, BNW, WAVES_M, WAVES_N, false, BK, NS, MINW, true, true>),
+                           grid, block_pc, 0, s, p);
+      else if (sw)
+        hipLaunchKernelGGL((grouped_gemm_kernel<BM, BNW, WAVES_M, WAVES_N, true, BK, NS, MINW, false, true>),
+                           grid, block_pc, 0, s, p);
+      else
+        hipLaunchKernelGGL((grouped_gemm_kernel<BM, BNW, WAVES_M, WAVES_N, false, BK, NS, MINW, false, true>),
+                           grid, block_pc, 0, s, p);
+      return hipGetLastError();
+    }
+  }
   if (wnt && sw)
     hipLaunchKernelGGL((grouped_gemm_kernel<BM, BNW, WAVES_M, WAVES_N, true, BK, NS, MINW, BM == 128>),
                        grid, block, 0, s, p);
@@ -778,6 +984,9 @@ hipError_t launch_bm(GemmParams p, hipStream_t s) {
 
 // Tile configurations per BLOCK_M (compile-time knobs, defaults tuned on MI355X):
 // BM, BNW, WAVES_M, WAVES_N, BK, NS, MINW.
+#ifndef MOE_G256
+#define MOE_G256 256, 256, 2, 4, 64, 2, 1
+#endif
 #ifndef MOE_G128
 #define MOE_G128 128, 256, 2, 4, 64, 3, 1
 #endif
@@ -793,6 +1002,7 @@ hipError_t launch_bm(GemmParams p, hipStream_t s) {
 
 hipError_t launch_grouped_gemm(const GemmParams& p, int block_m, hipStream_t s) {
   switch (block_m) {
+    case 256: return launch_bm<MOE_G256>(p, s);
     case 128: return launch_bm<MOE_G128>(p, s);
     case 64: return launch_bm<MOE_G64>(p, s);
     case 32: return launch_bm<MOE_G32>(p, s);

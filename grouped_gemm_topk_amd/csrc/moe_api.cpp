@@ -44,7 +44,7 @@ constexpr int64_t kMaxBufferBytes = moe::kNoRowOffset;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
-bool valid_bm(int bm) { return bm == 16 || bm == 32 || bm == 64 || bm == 128; }
+bool valid_bm(int bm) { return bm == 16 || bm == 32 || bm == 64 || bm == 128 || bm == 256; }
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 

@@ -85,11 +85,13 @@ CONFIGS: Dict[str, MoEConfig] = {
                            logits_mode="dup3"),
     "decode_t8": MoEConfig("decode_t8", 2, T=8, H=2048, I=768, E=128, top_k=8, block_m=16),
     # DeepSeek-V3-8B-shaped: grouped sigmoid routing plus one shared expert
+    # (BLOCK_M 256: 2-4 % faster per layer than 128 on MI355X; 18 experts with
+    # about 900 slots each pad little)
     "dsv3": MoEConfig("dsv3", 3, T=4096, H=3072, I=2560, E=18, top_k=4,
-                      scoring=SCORE_SIGMOID, n_group=6, topk_group=4, n_shared=1, block_m=128),
+                      scoring=SCORE_SIGMOID, n_group=6, topk_group=4, n_shared=1, block_m=256),
     "dsv3_s2.5": MoEConfig("dsv3_s2.5", 3, T=4096, H=3072, I=2560, E=18, top_k=4,
                            scoring=SCORE_SIGMOID, n_group=6, topk_group=4, n_shared=1,
-                           scale=2.5, block_m=128),
+                           scale=2.5, block_m=256),
     # 128 experts with a Zipf(1.1) popularity prior (BLOCK_M 128: measured faster
     # than 64 despite the extra padding, fewer weight-tile passes)
     "zipf128": MoEConfig("zipf128", 4, T=8192, H=2816, I=704, E=128, top_k=8, block_m=128,

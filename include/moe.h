@@ -81,7 +81,7 @@ int64_t moe_align_capacity(int32_t T, int32_t k, int32_t E, int32_t block_m);
  * expert-id / padded-count triple of *Grouped GEMM Structure*).
  *
  *   topk_ids                int32 [T, k]   expert of each slot, 0 <= id < E
- *   block_m                 16, 32, 64 or 128
+ *   block_m                 16, 32, 64, 128 or 256
  *   sorted_token_ids  (out) int32 [capacity]: for expert e with c_e slots, its
  *                           padded range [o_e, o_e + p_e) (p_e = ceil(c_e/bm)*bm,
  *                           0 when c_e = 0; o_e = sum of p over lower experts)
@@ -193,7 +193,7 @@ int moe_grouped_gemm_backward(const moe_gemm_backward_args* args, void* workspac
  */
 typedef struct {
   int32_t T, H, I, E, top_k;
-  int32_t block_m;        /* 16, 32, 64 or 128                                            */
+  int32_t block_m;        /* 16, 32, 64, 128 or 256                                       */
   int32_t scoring;        /* MOE_SCORE_SOFTMAX or MOE_SCORE_SIGMOID                       */
   int32_t n_group;        /* expert groups (1 = no grouping); E % n_group == 0            */
   int32_t topk_group;     /* groups kept per token                                        */

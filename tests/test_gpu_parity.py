@@ -51,7 +51,7 @@ def _run_fused(moe, cfg, inp, block_m=None):
 
 
 # ---------------------------------------------------------------- align
-@pytest.mark.parametrize("bm", [16, 32, 64, 128])
+@pytest.mark.parametrize("bm", [16, 32, 64, 128, 256])
 @pytest.mark.parametrize("T,k,E,mode", [
     (1, 8, 128, "rand"), (3, 8, 128, "rand"), (37, 2, 8, "rand"), (64, 2, 8, "rand"),
     (100, 4, 18, "rand"), (513, 6, 128, "rand"), (700, 8, 256, "rand"),
@@ -86,7 +86,7 @@ def test_align_bit_exact(moe, T, k, E, mode, bm):
 
 
 # ---------------------------------------------------------------- grouped GEMM
-@pytest.mark.parametrize("bm", [16, 32, 64, 128])
+@pytest.mark.parametrize("bm", [16, 32, 64, 128, 256])
 @pytest.mark.parametrize("epi,c32", [(O.EPI_STORE, 1), (O.EPI_STORE, 0), (O.EPI_SWIGLU, 0),
                                      (O.EPI_RELU2, 0), (O.EPI_WEIGHTED_SCATTER, 1),
                                      (O.EPI_SWIGLU, 1)])
@@ -185,7 +185,7 @@ SMALL = [
 
 
 @pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
-@pytest.mark.parametrize("bm", [None, 16, 128])
+@pytest.mark.parametrize("bm", [None, 16, 128, 256])
 def test_fused_forward_small(moe, cfg, bm):
     print(f"fused {cfg.name} bm={bm}", flush=True)
     inp = W.make_inputs(cfg)
@@ -222,14 +222,16 @@ def test_fused_forward_zero_tokens(moe):
 
 
 # ---------------------------------------------------------------- full-size configs
-def _full_case(moe, name):
+def _full_case(moe, name, bm=None):
     """Every config at its full size in the launch configuration the benchmark
     times: routing bit-exact and the whole [T, H] output against the oracle's
     layer (a per-expert loop over all tokens)."""
     cfg = W.CONFIGS[name]
-    print(f"full-size {name}", flush=True)
+    if bm is not None:
+        cfg = dataclasses.replace(cfg, block_m=bm)
+    print(f"full-size {name} bm={cfg.block_m}", flush=True)
     inp = W.make_inputs(cfg)
-    out, routing = _run_fused(moe, cfg, inp)
+    out, routing = _run_fused(moe, cfg, inp, bm)
     ref = O.moe_forward_cfg(cfg, inp)
     _check_routing(routing, ref, cfg.T, cfg.top_k, cfg.block_m)
     max_abs, rel = assert_out_close(out, ref["out"], name)
@@ -244,3 +246,10 @@ def test_full_decode_configs(moe, name):
 @pytest.mark.parametrize("name", ["dsv3", "dsv3_s2.5", "zipf128", "relu2_t2048"])
 def test_full_prefill_configs(moe, name):
     _full_case(moe, name)
+
+
+@pytest.mark.parametrize("name,bm", [("dsv3", 128), ("dsv3", 256), ("zipf128", 128),
+                                     ("zipf128", 256), ("relu2_t2048", 256)])
+def test_full_prefill_block_m(moe, name, bm):
+    """The full-size prefill layers laid out at the other large BLOCK_M."""
+    _full_case(moe, name, bm)

@@ -1,5 +1,5 @@
-"""Parity of the layer on the less common paths of the persistent 128-row
-grouped GEMM (one workgroup per CU running a sequence of tiles).
+"""Parity of the layer on the less common paths of the persistent 128- and
+256-row grouped GEMM (one workgroup per CU running a sequence of tiles).
 
 - more than 2048 routed m-blocks: the expert ids no longer fit the LDS copy
   and the tile mapping reads them from global memory;
@@ -40,6 +40,12 @@ CASES = [
                    scoring=W.SCORE_SIGMOID, n_group=2, topk_group=2, n_shared=1),
     # one expert, top-1: 128 m-blocks x 4 n-tiles = 512 tiles, two per CU
     W.small_config("p_exact_rounds", T=16384, H=64, I=512, E=1, top_k=1, block_m=128),
+    # the same paths with 256-row tiles: 528000 slots, about 2070 m-blocks of 256
+    W.small_config("p_many_blocks_256", T=66000, H=64, I=32, E=8, top_k=8, block_m=256),
+    W.small_config("p_ragged_k_shared_256", T=8192, H=200, I=512, E=4, top_k=2, block_m=256,
+                   scoring=W.SCORE_SIGMOID, n_group=2, topk_group=2, n_shared=1),
+    # 64 m-blocks x 4 n-tiles = 256 tiles, one per CU
+    W.small_config("p_exact_rounds_256", T=16384, H=64, I=512, E=1, top_k=1, block_m=256),
 ]
 
 
@@ -56,7 +62,7 @@ def test_persistent_gemm_paths(moe, cfg):
     assert np.array_equal(r["topk_ids"].cpu().numpy(), ref["topk_ids"])
     ntpp = int(r["num_tokens_post_padded"].cpu().item())
     assert ntpp == ref["num_tokens_post_padded"]
-    if cfg.name == "p_many_blocks":
+    if cfg.name.startswith("p_many_blocks"):
         assert ntpp // cfg.block_m > 2048
     assert np.array_equal(r["sorted_token_ids"].cpu().numpy()[:ntpp], ref["sorted_token_ids"])
     assert np.array_equal(r["expert_ids"].cpu().numpy()[:ntpp // cfg.block_m], ref["expert_ids"])

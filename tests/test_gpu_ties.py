@@ -129,7 +129,7 @@ def test_ties_grouped_sigmoid(moe, E, n_group, topk_group, k, T, mode):
 def test_ties_block_m_sweep(moe, T):
     """The same tied routing laid out at every BLOCK_M."""
     logits = W.make_tie_logits(T, 16, 3, "coarse", seed=7)
-    for bm in (16, 32, 64, 128):
+    for bm in (16, 32, 64, 128, 256):
         print(f"ties bm sweep T={T} bm={bm}", flush=True)
         cfg = W.small_config(f"ties_bm_{T}_{bm}", T=T, H=64, I=32, E=16, top_k=3, block_m=bm)
         _run_case(moe, cfg, logits)
