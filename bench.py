@@ -47,6 +47,12 @@ PREFILL_CASES = ("zipf128", "relu2_t2048")
 # WRITE_SIZE x 1.0, the factors that turn the same counters into the known
 # bytes of a 1 GiB device copy.  Valid only for the kernel source with this
 # digest; any other source reports traffic null until it is measured again.
+# the SwiGLU grouped GEMM instantiation a layer of each BLOCK_M launches
+DOMINANT_KERNEL = {
+    256: "grouped_gemm_kernel<256, 256, 2, 4, true, 64, 2, 1, false, false>",
+    128: "grouped_gemm_kernel<128, 256, 2, 4, true, 64, 3, 1, false, true>",
+}
+
 DOMINANT_TRAFFIC = {
     "src": "grouped_gemm_topk_amd/csrc/gemm.hip",
     "sha256": "fa1da8ccf8879d2719b99ff2fc3b5d337a561339da519df127feb9f9cd525092",
@@ -675,7 +681,7 @@ def main():
                    "mfma_frac_of_layer": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                    "wall_s_timed": round(wall, 3),
                    "step_ms_spread": spread},
-        "roofline": {"bound": "mfma", "kernel": "grouped_gemm_kernel<128, 256, 2, 4, true, 64, 3, 1> (routed W13 + SwiGLU)",
+        "roofline": {"bound": "mfma", "kernel": f"{DOMINANT_KERNEL.get(cfg.block_m, 'grouped_gemm_kernel')} (routed W13 + SwiGLU)",
                      "achieved": round(gemm_tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tf / MFMA_BF16_PEAK_TFLOPS, 4),
                      "traffic": dominant_traffic(cfg.name),
