@@ -55,10 +55,10 @@ DOMINANT_KERNEL = {
 
 DOMINANT_TRAFFIC = {
     "src": "grouped_gemm_topk_amd/csrc/gemm.hip",
-    "sha256": "fa1da8ccf8879d2719b99ff2fc3b5d337a561339da519df127feb9f9cd525092",
+    "sha256": "46f28004b2f0c8956a9dabc50ab6c2c2cb9bedf40b2e346ef62dae4c97da9aca",
     "config": "dsv3",
-    "fetch_bytes": 898857920,
-    "write_bytes": 94400251,
+    "fetch_bytes": 898851883,
+    "write_bytes": 94405845,
 }
 
 
