@@ -7,7 +7,9 @@
   tile's first K steps are requested between the tiles, not ahead;
 - a ragged last K step with several tiles per workgroup and the shared
   expert's dense tiles after the routed ones;
-- a tile count that is an exact multiple of the CU count.
+- a tile count that is an exact multiple of the CU count;
+- two K steps per tile (with the loader waves of the 128-row tile, a tile's
+  sorted ids are read three tiles after they are written).
 
 Routing outputs bit for bit, the output at the layer's bar (max|d| <= 2e-2,
 relative-L2 <= 5e-3), against the oracle on the whole output.
@@ -40,6 +42,13 @@ CASES = [
                    scoring=W.SCORE_SIGMOID, n_group=2, topk_group=2, n_shared=1),
     # one expert, top-1: 128 m-blocks x 4 n-tiles = 512 tiles, two per CU
     W.small_config("p_exact_rounds", T=16384, H=64, I=512, E=1, top_k=1, block_m=128),
+    # two K steps per tile (ragged K = 104, then K = 120), several tiles per
+    # workgroup: the W13 launch (5 n-tiles x 259 m-blocks), then the W2
+    # launch (3 n-tiles x 514 m-blocks); with the loader waves a tile's sorted
+    # ids are read three tiles after they are written
+    W.small_config("p_two_steps_w13", T=16384, H=104, I=520, E=4, top_k=2, block_m=128),
+    W.small_config("p_two_steps_w2", T=32768, H=520, I=120, E=4, top_k=2, block_m=128),
+    W.small_config("p_two_steps_w13_256", T=16384, H=104, I=520, E=4, top_k=2, block_m=256),
     # the same paths with 256-row tiles: 528000 slots, about 2070 m-blocks of 256
     W.small_config("p_many_blocks_256", T=66000, H=64, I=32, E=8, top_k=8, block_m=256),
     W.small_config("p_ragged_k_shared_256", T=8192, H=200, I=512, E=4, top_k=2, block_m=256,
