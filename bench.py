@@ -409,8 +409,10 @@ def _interleaved_ms(fns, steps, warmup, torch, rounds=5):
 def gemm_scenarios(steps, warmup, torch, moe, W):
     """The contiguous grouped GEMM at the four shapes of the axolotl page's
     benchmark table (uniform groups): the whole call (align of the per-row
-    indices + grouped GEMM) and the GEMM launch alone, plus hipBLASLt (one
-    torch.matmul per group on a contiguous transposed weight) as context; then
+    indices + grouped GEMM), the GEMM launch alone with the persistent grid
+    and with one workgroup per tile (the page's table times its persistent and
+    its non-persistent kernel side by side), plus hipBLASLt (one torch.matmul
+    per group on a contiguous transposed weight) as context; then
     the backward (input and weight gradients, each with its layout kernels)
     beside hipBLASLt per group.  Timed in alternation over five rounds; medians."""
     res = []
@@ -428,7 +430,9 @@ def gemm_scenarios(steps, warmup, torch, moe, W):
         def blas():
             for g in range(sc.G):
                 torch.matmul(xs[g], wt[g], out=outs[g])
-        ms_call, ms_gemm, ms_blas = _interleaved_ms([op.run, op.gemm, blas], steps, warmup, torch)
+        per_tile = lambda: op.gemm(schedule=moe.SCHED_PER_TILE)
+        ms_call, ms_gemm, ms_tile, ms_blas = _interleaved_ms([op.run, op.gemm, per_tile, blas],
+                                                             steps, warmup, torch)
         # backward: dx (weight transpose + grouped GEMM) and dw (segment table,
         # gathered transposes of dy and x + segmented GEMM), each 2 M N K flops
         dy = _to_dev(W.make_gemm_inputs(sc, with_grad=True)["dy"], torch)
@@ -458,6 +462,8 @@ def gemm_scenarios(steps, warmup, torch, moe, W):
                     "gemm_ms": round(ms_gemm, 4),
                     "gemm_TFLOPS": round(f / (ms_gemm * 1e-3) / 1e12, 1),
                     "mfma_frac": round(f / (ms_gemm * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                    "gemm_per_tile_ms": round(ms_tile, 4),
+                    "gemm_per_tile_TFLOPS": round(f / (ms_tile * 1e-3) / 1e12, 1),
                     "hipblaslt_per_group_ms": round(ms_blas, 4),
                     "hipblaslt_per_group_TFLOPS": round(f / (ms_blas * 1e-3) / 1e12, 1),
                     "backward": {

@@ -933,7 +933,7 @@ hipError_t launch_bm(GemmParams p, hipStream_t s) {
   // one workgroup per CU (the LDS of the 128- and 256-row tiles admits no second one),
   // each running tiles gridDim.x apart; the CU count is a multiple of 8, so a
   // workgroup stays on the XCD its tiles are numbered for
-  if (BM >= 128 && p.nseg == 0) {
+  if (BM >= 128 && p.nseg == 0 && !p.per_tile) {
     const int ncu = cu_count();
     if (ncu > 0 && ncu % 8 == 0 && nwg > ncu) nwg = ncu;
   }
@@ -948,7 +948,7 @@ hipError_t launch_bm(GemmParams p, hipStream_t s) {
   const dim3 grid((unsigned)nwg), block(64 * WAVES_M * WAVES_N);
   if constexpr (BM == 128 && NS == 3) {
     // persistent 128-row tiles with one K: the loader / compute split
-    if (p.nseg == 0 && MOE_PC) {
+    if (p.nseg == 0 && MOE_PC && !p.per_tile) {
       const dim3 block_pc(64 * (WAVES_M * WAVES_N + MOE_NLW));
       if (wnt && sw)
         hipLaunchKernelGGL((grouped_gemm_kernel<BM, BNW, WAVES_M, WAVES_N, true, BK, NS, MINW, true, true>),

@@ -217,6 +217,7 @@ int moe_grouped_gemm(const moe_gemm_args* args, void* workspace, size_t* workspa
   if (g.num_valid < 0 || g.a_row_div < 0) return MOE_ERR_SHAPE;
   if (g.a_row_div > 0 && g.num_valid % g.a_row_div != 0) return MOE_ERR_SHAPE;
   if (g.c_is_fp32 != 0 && g.c_is_fp32 != 1) return MOE_ERR_SHAPE;
+  if (g.schedule != MOE_SCHED_PERSISTENT && g.schedule != MOE_SCHED_PER_TILE) return MOE_ERR_SHAPE;
   {  // byte offsets inside one A matrix and one expert's W are 32-bit
     const int64_t a_rows = g.a_row_div > 0 ? g.num_valid / g.a_row_div : g.capacity;
     if (a_rows * g.K * 2 >= kMaxBufferBytes || (int64_t)g.N * g.K * 2 >= kMaxBufferBytes)
@@ -250,6 +251,7 @@ int moe_grouped_gemm(const moe_gemm_args* args, void* workspace, size_t* workspa
   p.ldc = g.epilogue == MOE_EPI_SWIGLU ? g.N / 2 : g.N;
   p.a_rows = g.a_row_div > 0 ? g.num_valid / g.a_row_div : g.capacity;
   p.lda = p.ldw = g.K;
+  p.per_tile = g.schedule == MOE_SCHED_PER_TILE;
   return hip_status(moe::launch_grouped_gemm(p, g.block_m, (hipStream_t)stream));
 }
 

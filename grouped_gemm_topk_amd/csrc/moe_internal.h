@@ -85,6 +85,9 @@ struct GemmParams {
   const int* seg_beg;
   const int* seg_end;
   int64_t seg_c_stride;
+  // one workgroup per tile instead of the persistent grid of the 128- and
+  // 256-row tiles (same results; for comparisons)
+  int per_tile;
 };
 
 // ---------------------------------------------------------------- decode GEMVs

@@ -22,6 +22,7 @@ MOE_OK = 0
 SCORE_SOFTMAX, SCORE_SIGMOID = 0, 1
 ACT_SWIGLU, ACT_RELU2 = 0, 1
 EPI_STORE, EPI_SWIGLU, EPI_RELU2, EPI_WEIGHTED_SCATTER = 0, 1, 2, 3
+SCHED_PERSISTENT, SCHED_PER_TILE = 0, 1
 
 EXPORTED = ("moe_align", "moe_grouped_gemm", "moe_grouped_gemm_backward", "moe_fused_forward",
             "moe_fused_forward_mxfp8", "moe_fused_forward_router", "moe_fused_forward_noalloc",
@@ -52,7 +53,7 @@ class MoeGemmArgs(ctypes.Structure):
                 ("num_tokens_post_padded", ctypes.c_void_p), ("block_m", ctypes.c_int32),
                 ("num_valid", ctypes.c_int32), ("capacity", ctypes.c_int32),
                 ("epilogue", ctypes.c_int32), ("topk_weights", ctypes.c_void_p),
-                ("c", ctypes.c_void_p), ("c_is_fp32", ctypes.c_int32)]
+                ("c", ctypes.c_void_p), ("c_is_fp32", ctypes.c_int32), ("schedule", ctypes.c_int32)]
 
 
 class MoeGemmBackwardArgs(ctypes.Structure):
@@ -176,8 +177,9 @@ def moe_grouped_gemm(a: torch.Tensor, a_row_div: int, w: torch.Tensor,
                      sorted_token_ids: torch.Tensor, expert_ids: torch.Tensor,
                      num_tokens_post_padded: torch.Tensor, block_m: int, num_valid: int,
                      epilogue: int, c: torch.Tensor, topk_weights: Optional[torch.Tensor] = None,
-                     stream=None) -> torch.Tensor:
-    """One grouped GEMM over the aligned layout; writes and returns ``c``."""
+                     stream=None, schedule: int = 0) -> torch.Tensor:
+    """One grouped GEMM over the aligned layout; writes and returns ``c``.
+    ``schedule``: SCHED_PERSISTENT (default) or SCHED_PER_TILE."""
     _dev(a, "a", torch.bfloat16)
     _dev(w, "w", torch.bfloat16)
     E, N, K = w.shape
@@ -196,7 +198,7 @@ def moe_grouped_gemm(a: torch.Tensor, a_row_div: int, w: torch.Tensor,
                        num_tokens_post_padded=_ptr(num_tokens_post_padded), block_m=block_m,
                        num_valid=num_valid, capacity=sorted_token_ids.numel(), epilogue=epilogue,
                        topk_weights=_ptr(topk_weights), c=_ptr(c),
-                       c_is_fp32=1 if c.dtype == torch.float32 else 0)
+                       c_is_fp32=1 if c.dtype == torch.float32 else 0, schedule=schedule)
     n = ctypes.c_size_t(0)
     _check("moe_grouped_gemm", lib().moe_grouped_gemm(ctypes.byref(args), None, ctypes.byref(n),
                                                       _stream(stream)))
@@ -240,9 +242,10 @@ class IndexedGroupedGemm:
         moe_align(self.ids, self.G, self.block_m, self.sorted, self.expert_ids, self.ntpp,
                   self.workspace, stream)
 
-    def gemm(self, stream=None) -> torch.Tensor:
+    def gemm(self, stream=None, schedule: int = 0) -> torch.Tensor:
         return moe_grouped_gemm(self.x, 1, self.w, self.sorted, self.expert_ids, self.ntpp,
-                                self.block_m, self.M, EPI_WEIGHTED_SCATTER, self.out, None, stream)
+                                self.block_m, self.M, EPI_WEIGHTED_SCATTER, self.out, None, stream,
+                                schedule)
 
     def run(self, stream=None) -> torch.Tensor:
         self.align(stream)

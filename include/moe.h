@@ -60,6 +60,13 @@ enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 };
 enum { MOE_ACT_SWIGLU = 0, MOE_ACT_RELU2 = 1 };
 enum { MOE_EPI_STORE = 0, MOE_EPI_SWIGLU = 1, MOE_EPI_RELU2 = 2, MOE_EPI_WEIGHTED_SCATTER = 3 };
 
+/* Tile schedules of moe_grouped_gemm (same results, bit for bit): at
+ * BLOCK_M 128 and 256 one workgroup per compute unit runs a sequence of tiles
+ * (PERSISTENT, the default), or one workgroup per tile (PER_TILE; the
+ * axolotl page's benchmark times its persistent and its non-persistent
+ * kernels side by side). */
+enum { MOE_SCHED_PERSISTENT = 0, MOE_SCHED_PER_TILE = 1 };
+
 /* Limits enforced by validation. */
 #define MOE_MAX_EXPERTS 256
 #define MOE_MAX_TOPK 16
@@ -135,6 +142,7 @@ typedef struct {
   const float* topk_weights; /* [num_valid] for WEIGHTED_SCATTER, or NULL (weight 1)     */
   void* c;                 /* output rows: capacity rows (row-ordered) or num_valid rows */
   int32_t c_is_fp32;       /* 1: fp32 output, 0: bf16 (round to nearest even)            */
+  int32_t schedule;        /* MOE_SCHED_*; 0 (the default) = persistent                  */
 } moe_gemm_args;
 
 int moe_grouped_gemm(const moe_gemm_args* args, void* workspace, size_t* workspace_bytes,

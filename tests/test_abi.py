@@ -153,6 +153,8 @@ def test_grouped_gemm_validation(L):
     assert call(N=60) == -2
     assert call(epilogue=1, N=56) == -2
     assert call(epilogue=4) == -2
+    assert call(schedule=2) == -2          # MOE_SCHED_* only
+    assert call(schedule=-1) == -2
     assert call(block_m=48) == -2
     assert call(capacity=100) == -2
     assert call(E=0) == -2

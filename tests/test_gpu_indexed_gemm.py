@@ -87,6 +87,39 @@ def test_indexed_grouped_gemm_reuse_and_new_indices(moe):
 FULL = list(W.GEMM_SCENARIOS.values())
 
 
+SCHED = [
+    # more tiles than CUs, so that the persistent grid runs tile sequences:
+    # 190 m-blocks x 3 n-tiles at BLOCK_M 128, 120 x 4 at 256 (ragged K)
+    W.small_gemm_scenario("sched_bm128", G=6, M=6 * 4000, N=520, K=264, block_m=128),
+    W.small_gemm_scenario("sched_bm256", G=5, M=5 * 6000, N=1000, K=200, block_m=256),
+    W.small_gemm_scenario("sched_bm64", G=8, M=8 * 70, N=136, K=264, block_m=64),
+]
+
+
+@pytest.mark.parametrize("sc", SCHED, ids=[s.name for s in SCHED])
+def test_indexed_grouped_gemm_schedules(moe, sc):
+    """One workgroup per tile (MOE_SCHED_PER_TILE) against the persistent
+    default: the same output bit for bit, and both against the oracle."""
+    print(f"indexed grouped gemm schedules {sc.name}", flush=True)
+    inp = W.make_gemm_inputs(sc)
+    ref = O.indexed_grouped_gemm(O.bf16_to_f64(inp["x"]), O.bf16_to_f64(inp["w"]),
+                                 inp["expert_indices"])
+    outs = []
+    for sched in (moe.SCHED_PERSISTENT, moe.SCHED_PER_TILE):
+        out = torch.full((sc.M, sc.N), float("nan"), device="cuda", dtype=torch.float32)
+        op = moe.IndexedGroupedGemm(to_dev(inp["x"]), to_dev(inp["w"]),
+                                    to_dev(inp["expert_indices"]), sc.block_m, out)
+        op.align()
+        op.gemm(schedule=sched)
+        torch.cuda.synchronize()
+        outs.append(out.cpu().numpy())
+    for got in outs:
+        assert np.all(np.isfinite(got)), "rows left unwritten"
+        bad = np.abs(got - ref) > _tol(ref, True)
+        assert not bad.any(), f"{bad.sum()} mismatches, worst {np.abs(got - ref).max()}"
+    assert np.array_equal(outs[0], outs[1]), "the schedules disagree"
+
+
 @pytest.mark.parametrize("sc", FULL, ids=[s.name for s in FULL])
 def test_indexed_grouped_gemm_full_size_sampled(moe, sc):
     print(f"indexed grouped gemm full size {sc.name}", flush=True)
