@@ -55,10 +55,10 @@ DOMINANT_KERNEL = {
 
 DOMINANT_TRAFFIC = {
     "src": "grouped_gemm_topk_amd/csrc/gemm.hip",
-    "sha256": "46f28004b2f0c8956a9dabc50ab6c2c2cb9bedf40b2e346ef62dae4c97da9aca",
+    "sha256": "96d4bb32224a55e23bfc5aaf847c8c39f2ce47aa38831b6d41c08d592f1aeaa7",
     "config": "dsv3",
-    "fetch_bytes": 898851883,
-    "write_bytes": 94405845,
+    "fetch_bytes": 898846315,
+    "write_bytes": 94408512,
 }
 
 
