@@ -219,7 +219,25 @@ __global__ void __launch_bounds__(64 * (WAVES_M * WAVES_N + (PC ? MOE_NLW : 0)),
     vbr = min(pin.mblocks, ((pin.ntpp ? *pin.ntpp : pin.M) + BM - 1) / BM);
     nvalid = ntn * (vbr + pin.nsb);
   }
-  if ((int)blockIdx.x >= nvalid) return;
+  // nrun: the launch-sequence indices this launch runs.  A persistent launch
+  // whose last round would fill at most half the grid stops after its full
+  // rounds (tail 1); a second launch (tail 2) runs the tiles of that round
+  // cut into tail_s slices of its own, narrower tile width, one per
+  // workgroup, so that the last round's few tiles are spread over all CUs.
+  int nrun = nvalid, tail_base = 0;
+  if (pin.tail) {
+    const int gm = pin.main_grid;
+    const int rem = nvalid % gm;
+    const bool split = nvalid > gm && rem > 0 && 2 * rem <= gm;
+    if (pin.tail == 1) {
+      if (split) nrun = nvalid - rem;
+    } else {
+      if (!split) return;
+      tail_base = nvalid - rem;
+      nrun = rem * pin.tail_s;
+    }
+  }
+  if ((int)blockIdx.x >= nrun) return;
   const int G = gridDim.x;
   const int ncols = SW ? pin.I : pin.N;   // output columns
   constexpr int GM = MOE_GM;
@@ -248,12 +266,18 @@ __global__ void __launch_bounds__(64 * (WAVES_M * WAVES_N + (PC ? MOE_NLW : 0)),
   // a tile's place: m-block, n-tile, expert (the segment in segmented launches)
   struct Map {
     int mb, nt, e;
+    int slice;            // slice of the n-tile (slice launches)
     bool second, store;   // dense second part; false only for an invalid expert id
   };
   auto resolve = [&](int Lt) -> Map {
     Map m;
     m.store = true;
     m.second = false;
+    m.slice = 0;
+    if (pin.tail == 2) {   // a slice of a tile of the main launch's last round
+      m.slice = Lt % pin.tail_s;
+      Lt = tail_base + Lt / pin.tail_s;
+    }
     const int tg = xcd_tile(Lt, nvalid);
     if (pin.nseg > 0) {
       // segmented reduction: segment s is a dense product over its own columns
@@ -303,7 +327,8 @@ __global__ void __launch_bounds__(64 * (WAVES_M * WAVES_N + (PC ? MOE_NLW : 0)),
     Tile t;
     t.store = m.store;
     t.m0 = m.mb * BM;
-    t.n0 = m.nt * (SW ? BNW / 2 : BNW);
+    t.n0 = pin.tail == 2 ? m.nt * pin.main_tile_n + m.slice * (SW ? BNW / 2 : BNW)
+                         : m.nt * (SW ? BNW / 2 : BNW);
     t.K = pin.K;
     if (pin.nseg > 0) {
       const int beg = pin.seg_beg[m.e];
@@ -684,7 +709,7 @@ __global__ void __launch_bounds__(64 * (WAVES_M * WAVES_N + (PC ? MOE_NLW : 0)),
     constexpr int R = 4;
     __shared__ int s_ids[R][BM];
     const int L0 = blockIdx.x;
-    const int ntl = (nvalid - L0 + G - 1) / G;   // tiles of this workgroup (>= 1)
+    const int ntl = (nrun - L0 + G - 1) / G;   // tiles of this workgroup (>= 1)
     const int nk = (K + BK - 1) / BK;
     const int C = ntl * nk;
     const int J = nk >= 3 ? 2 : (nk == 2 ? 3 : 4);   // (J - 1) * nk >= 3, J <= R
@@ -828,7 +853,7 @@ __global__ void __launch_bounds__(64 * (WAVES_M * WAVES_N + (PC ? MOE_NLW : 0)),
     // the second tile: mapping and row ids
     int Ln = L + G;
     Tile nxt = cur;
-    if (Ln < nvalid) {
+    if (Ln < nrun) {
       nxt = tile_of(resolve(Ln));
       load_ids(nxt, xs, es);
     }
@@ -874,7 +899,7 @@ __global__ void __launch_bounds__(64 * (WAVES_M * WAVES_N + (PC ? MOE_NLW : 0)),
       float dsc[FM];
   #pragma unroll
       for (int q = 0; q < FM; ++q) dsc[q] = sc[q];
-      const bool more = Ln < nvalid;
+      const bool more = Ln < nrun;
       if (more) {
         // the next tile: its first D steps, then its routed weights
         cur = nxt;
@@ -887,7 +912,7 @@ __global__ void __launch_bounds__(64 * (WAVES_M * WAVES_N + (PC ? MOE_NLW : 0)),
         load_scale(cur, er, sc);
         // the tile after it: mapping and row ids
         Ln += G;
-        if (Ln < nvalid) {
+        if (Ln < nrun) {
           nxt = tile_of(resolve(Ln));
           load_ids(nxt, xs, es);
         }
@@ -919,33 +944,10 @@ int cu_count() {
   return n;
 }
 
+// the main launch of launch_bm: the kernel instantiation for the tile and
+// its epilogue, non-temporal weights and the loader / compute split
 template <int BM, int BNW, int WAVES_M, int WAVES_N, int BK, int NS, int MINW>
-hipError_t launch_bm(GemmParams p, hipStream_t s) {
-  const bool sw = p.epi == 1;
-  const int ncols = sw ? p.I : p.N;
-  const int tile_n = sw ? BNW / 2 : BNW;
-  p.mblocks = (p.M + BM - 1) / BM;
-  p.nsb = p.M2 > 0 ? (p.M2 + BM - 1) / BM : 0;
-  p.ntiles_n = (ncols + tile_n - 1) / tile_n;
-  if (p.nseg > 0) p.nsb = 0;
-  int64_t nwg = (int64_t)(p.mblocks + p.nsb) * p.ntiles_n * (p.nseg > 0 ? p.nseg : 1);
-  if (nwg == 0) return hipSuccess;
-  // one workgroup per CU (the LDS of the 128- and 256-row tiles admits no second one),
-  // each running tiles gridDim.x apart; the CU count is a multiple of 8, so a
-  // workgroup stays on the XCD its tiles are numbered for
-  if (BM >= 128 && p.nseg == 0 && !p.per_tile) {
-    const int ncu = cu_count();
-    if (ncu > 0 && ncu % 8 == 0 && nwg > ncu) nwg = ncu;
-  }
-  // Experts that hold on average at most one m-block (T * top_k <= E * BM)
-  // use each weight tile in one tile only: with no dense second part (whose
-  // weights every m-block reads), the 128-row tile then streams its weight
-  // rows non-temporally, which keeps the token rows cached (relu2 at T = 2048,
-  // 128 experts top-6: 620 -> 589 us per layer; where experts hold several
-  // m-blocks the hint costs 6-10 %, so it is not used there)
-  const bool wnt = BM == 128 && p.nseg == 0 && p.M2 == 0 && p.expert_ids &&
-                   (int64_t)p.num_valid <= (int64_t)p.E * BM;
-  const dim3 grid((unsigned)nwg), block(64 * WAVES_M * WAVES_N);
+hipError_t launch_main(const GemmParams& p, dim3 grid, dim3 block, bool sw, bool wnt, hipStream_t s) {
   if constexpr (BM == 128 && NS == 3) {
     // persistent 128-row tiles with one K: the loader / compute split
     if (p.nseg == 0 && MOE_PC && !p.per_tile) {
@@ -978,6 +980,69 @@ hipError_t launch_bm(GemmParams p, hipStream_t s) {
     hipLaunchKernelGGL((grouped_gemm_kernel<BM, BNW, WAVES_M, WAVES_N, false, BK, NS, MINW>), grid,
                        block, 0, s, p);
   return hipGetLastError();
+}
+
+
+template <int BM, int BNW, int WAVES_M, int WAVES_N, int BK, int NS, int MINW>
+hipError_t launch_bm(GemmParams p, hipStream_t s) {
+  const bool sw = p.epi == 1;
+  const int ncols = sw ? p.I : p.N;
+  const int tile_n = sw ? BNW / 2 : BNW;
+  p.mblocks = (p.M + BM - 1) / BM;
+  p.nsb = p.M2 > 0 ? (p.M2 + BM - 1) / BM : 0;
+  p.ntiles_n = (ncols + tile_n - 1) / tile_n;
+  if (p.nseg > 0) p.nsb = 0;
+  int64_t nwg = (int64_t)(p.mblocks + p.nsb) * p.ntiles_n * (p.nseg > 0 ? p.nseg : 1);
+  if (nwg == 0) return hipSuccess;
+  // one workgroup per CU (the LDS of the 128- and 256-row tiles admits no second one),
+  // each running tiles gridDim.x apart; the CU count is a multiple of 8, so a
+  // workgroup stays on the XCD its tiles are numbered for
+  bool persistent = false;
+  if (BM >= 128 && p.nseg == 0 && !p.per_tile) {
+    const int ncu = cu_count();
+    if (ncu > 0 && ncu % 8 == 0 && nwg > ncu) {
+      nwg = ncu;
+      persistent = true;
+    }
+  }
+  // (the last-round split pays with 256-row tiles only: dsv3 layer
+  // 1083 -> 1058 us; with 128-row tiles the main launch's last round is
+  // short and overlaps the tile before it, and the split costs 2-3 %)
+  p.tail = persistent && BM == 256 ? 1 : 0;
+  p.main_grid = (int)nwg;
+  // Experts that hold on average at most one m-block (T * top_k <= E * BM)
+  // use each weight tile in one tile only: with no dense second part (whose
+  // weights every m-block reads), the 128-row tile then streams its weight
+  // rows non-temporally, which keeps the token rows cached (relu2 at T = 2048,
+  // 128 experts top-6: 620 -> 589 us per layer; where experts hold several
+  // m-blocks the hint costs 6-10 %, so it is not used there)
+  const bool wnt = BM == 128 && p.nseg == 0 && p.M2 == 0 && p.expert_ids &&
+                   (int64_t)p.num_valid <= (int64_t)p.E * BM;
+  const dim3 grid((unsigned)nwg), block(64 * WAVES_M * WAVES_N);
+  hipError_t e = launch_main<BM, BNW, WAVES_M, WAVES_N, BK, NS, MINW>(p, grid, block, sw, wnt, s);
+  if (e != hipSuccess || !p.tail) return e;
+  // the slices of a last round filling at most half the grid (each kernel
+  // decides from the tile count; with no such round the slice launch's
+  // workgroups return at once): eight waves of 32-row MFMA blocks, as in
+  // the main launch, so every output is the same bit for bit, in 64-column
+  // slices (32 act columns with SwiGLU)
+  if constexpr (BM == 256) {
+    constexpr int TWM = BM / 32, TWN = 1;   // one wave per 32-row block
+    constexpr int TB_SW = 64, TB = 64;      // slice tile widths in weight rows
+    GemmParams pt = p;
+    pt.tail = 2;
+    pt.main_tile_n = tile_n;
+    pt.tail_s = tile_n / (sw ? TB_SW / 2 : TB);
+    const dim3 tgrid((unsigned)(nwg / 2 * pt.tail_s)), tblock(64 * 8);
+    if (sw)
+      hipLaunchKernelGGL((grouped_gemm_kernel<BM, TB_SW, TWM, TWN, true, BK, 3, 1>), tgrid, tblock, 0,
+                         s, pt);
+    else
+      hipLaunchKernelGGL((grouped_gemm_kernel<BM, TB, TWM, TWN, false, BK, 3, 1>), tgrid, tblock, 0, s,
+                         pt);
+    return hipGetLastError();
+  }
+  return hipSuccess;
 }
 
 }  // namespace

@@ -88,6 +88,12 @@ struct GemmParams {
   // one workgroup per tile instead of the persistent grid of the 128- and
   // 256-row tiles (same results; for comparisons)
   int per_tile;
+  // set by the launcher: 1 in a persistent launch (which then leaves a last
+  // round filling at most half its grid to a second launch), 2 in that second
+  // launch, which cuts each of those tiles into tail_s slices of its own tile
+  // width; main_grid = the persistent launch's grid, main_tile_n = its tile
+  // width in output columns
+  int tail, tail_s, main_grid, main_tile_n;
 };
 
 // ---------------------------------------------------------------- decode GEMVs
