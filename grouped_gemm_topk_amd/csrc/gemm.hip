@@ -220,15 +220,18 @@ __global__ void __launch_bounds__(64 * (WAVES_M * WAVES_N + (PC ? MOE_NLW : 0)),
     nvalid = ntn * (vbr + pin.nsb);
   }
   // nrun: the launch-sequence indices this launch runs.  A persistent launch
-  // whose last round would fill at most half the grid stops after its full
-  // rounds (tail 1); a second launch (tail 2) runs the tiles of that round
-  // cut into tail_s slices of its own, narrower tile width, one per
-  // workgroup, so that the last round's few tiles are spread over all CUs.
+  // whose last round would fill at most a quarter of the grid stops after its
+  // full rounds (tail 1); a second launch (tail 2) runs the tiles of that
+  // round cut into tail_s slices of its own, narrower tile width, one per
+  // workgroup, so that the last round's few tiles are spread over the CUs.
+  // (A quarter: the slices then fit in one round.  On the dsv3 layer's W2, a
+  // last round of 44 tiles took 72 us and its 176 slices take 43 us; two
+  // rounds of slices would cost about what a half-full last round does.)
   int nrun = nvalid, tail_base = 0;
   if (pin.tail) {
     const int gm = pin.main_grid;
     const int rem = nvalid % gm;
-    const bool split = nvalid > gm && rem > 0 && 2 * rem <= gm;
+    const bool split = nvalid > gm && rem > 0 && 4 * rem <= gm;
     if (pin.tail == 1) {
       if (split) nrun = nvalid - rem;
     } else {
@@ -1021,7 +1024,7 @@ hipError_t launch_bm(GemmParams p, hipStream_t s) {
   const dim3 grid((unsigned)nwg), block(64 * WAVES_M * WAVES_N);
   hipError_t e = launch_main<BM, BNW, WAVES_M, WAVES_N, BK, NS, MINW>(p, grid, block, sw, wnt, s);
   if (e != hipSuccess || !p.tail) return e;
-  // the slices of a last round filling at most half the grid (each kernel
+  // the slices of a last round filling at most a quarter of the grid (each kernel
   // decides from the tile count; with no such round the slice launch's
   // workgroups return at once): eight waves of 32-row MFMA blocks, as in
   // the main launch, so every output is the same bit for bit, in 64-column
@@ -1033,7 +1036,7 @@ hipError_t launch_bm(GemmParams p, hipStream_t s) {
     pt.tail = 2;
     pt.main_tile_n = tile_n;
     pt.tail_s = tile_n / (sw ? TB_SW / 2 : TB);
-    const dim3 tgrid((unsigned)(nwg / 2 * pt.tail_s)), tblock(64 * 8);
+    const dim3 tgrid((unsigned)(nwg / 4 * pt.tail_s)), tblock(64 * 8);
     if (sw)
       hipLaunchKernelGGL((grouped_gemm_kernel<BM, TB_SW, TWM, TWN, true, BK, 3, 1>), tgrid, tblock, 0,
                          s, pt);

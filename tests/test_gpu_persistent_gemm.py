@@ -10,10 +10,12 @@
 - a tile count that is an exact multiple of the CU count;
 - two K steps per tile (with the loader waves of the 128-row tile, a tile's
   sorted ids are read three tiles after they are written).
-- with 256-row tiles, a last round that fills at most half the grid: the
-  persistent launch stops after its full rounds and a second launch runs
-  that round's tiles in 64-column slices (both GEMMs, ragged K, and with
-  the shared expert's dense tiles in the sliced round).
+- with 256-row tiles, a last round that fills at most a quarter of the
+  grid: the persistent launch stops after its full rounds and a second
+  launch runs that round's tiles in 64-column slices (both GEMMs, ragged K,
+  the shared expert's dense tiles in the sliced round, and a layer whose
+  W13 launch keeps a last round of half the grid while its W2 launch
+  splits).
 
 Routing outputs bit for bit, the output at the layer's bar (max|d| <= 2e-2,
 relative-L2 <= 5e-3), against the oracle on the whole output.
@@ -59,11 +61,13 @@ CASES = [
                    scoring=W.SCORE_SIGMOID, n_group=2, topk_group=2, n_shared=1),
     # 64 m-blocks x 4 n-tiles = 256 tiles, one per CU
     W.small_config("p_exact_rounds_256", T=16384, H=64, I=512, E=1, top_k=1, block_m=256),
-    # on 256 CUs: W13 384 tiles (last round 128), W2 288 tiles (last round 32),
-    # K = 600 and 400 (ragged)
+    # on 256 CUs: W13 384 tiles (last round 128: not split), W2 288 tiles
+    # (last round 32: split), K = 600 and 400 (ragged)
     W.small_config("p_split_round_256", T=12000, H=600, I=400, E=4, top_k=2, block_m=256),
-    # W13 and W2 324 tiles each (last round 68, the shared expert's among them)
-    W.small_config("p_split_round_shared_256", T=9000, H=520, I=384, E=4, top_k=2, block_m=256,
+    # W13 and W2 280 tiles each (last rounds of 24 split), K = 1000 and 504
+    W.small_config("p_split_both_256", T=8600, H=1000, I=504, E=4, top_k=2, block_m=256),
+    # W13 and W2 312 tiles each (last rounds of 56, the shared expert's among them)
+    W.small_config("p_split_round_shared_256", T=8600, H=520, I=384, E=4, top_k=2, block_m=256,
                    scoring=W.SCORE_SIGMOID, n_group=2, topk_group=2, n_shared=1),
 ]
 
