@@ -237,7 +237,11 @@ __global__ void __launch_bounds__(64 * (WAVES_M * WAVES_N + (PC ? MOE_NLW : 0)),
     } else {
       if (!split) return;
       tail_base = nvalid - rem;
-      nrun = rem * pin.tail_s;
+      // one slice per workgroup (see resolve): this workgroup's slice exists
+      // when its tile does
+      const int i = ((int)blockIdx.x >> 3) / pin.tail_s;
+      if ((((int)blockIdx.x - tail_base) & 7) + 8 * i >= rem) return;
+      nrun = (int)blockIdx.x + 1;
     }
   }
   if ((int)blockIdx.x >= nrun) return;
@@ -277,9 +281,15 @@ __global__ void __launch_bounds__(64 * (WAVES_M * WAVES_N + (PC ? MOE_NLW : 0)),
     m.store = true;
     m.second = false;
     m.slice = 0;
-    if (pin.tail == 2) {   // a slice of a tile of the main launch's last round
-      m.slice = Lt % pin.tail_s;
-      Lt = tail_base + Lt / pin.tail_s;
+    if (pin.tail == 2) {
+      // a slice of a tile of the main launch's last round.  Workgroup Lt runs
+      // on XCD Lt mod 8: it takes a tile whose launch index is numbered for
+      // that XCD (index tail_base + j with j = Lt - tail_base mod 8), so that
+      // the slices of one tile, which read the same token rows, and the
+      // neighbouring tiles of that XCD's range share its L2
+      const int r = Lt >> 3, i = r / pin.tail_s;
+      m.slice = r - i * pin.tail_s;
+      Lt = tail_base + ((Lt - tail_base) & 7) + 8 * i;
     }
     const int tg = xcd_tile(Lt, nvalid);
     if (pin.nseg > 0) {
@@ -1036,7 +1046,9 @@ hipError_t launch_bm(GemmParams p, hipStream_t s) {
     pt.tail = 2;
     pt.main_tile_n = tile_n;
     pt.tail_s = tile_n / (sw ? TB_SW / 2 : TB);
-    const dim3 tgrid((unsigned)(nwg / 4 * pt.tail_s)), tblock(64 * 8);
+    // the last round holds at most nwg / 4 tiles, at most ceil(nwg / 32) per
+    // XCD, each in tail_s slices on its XCD's workgroups
+    const dim3 tgrid((unsigned)(8 * ((nwg + 31) / 32) * pt.tail_s)), tblock(64 * 8);
     if (sw)
       hipLaunchKernelGGL((grouped_gemm_kernel<BM, TB_SW, TWM, TWN, true, BK, 3, 1>), tgrid, tblock, 0,
                          s, pt);
