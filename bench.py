@@ -55,11 +55,11 @@ DOMINANT_KERNEL = {
 
 DOMINANT_TRAFFIC = {
     "src": "grouped_gemm_topk_amd/csrc/gemm.hip",
-    "sha256": "8f40b497beeafea6acf5b162d0c0921397da03afb2b1acdc9a47178bddc571ae",
+    "sha256": "8e409773b629967f1a052381216dc9663ec39e7fea3740ac0da7732b31b92e75",
     "config": "dsv3",
     # one call: the persistent launch and its (here empty) last-round slice launch
-    "fetch_bytes": 898906773,
-    "write_bytes": 94390928,
+    "fetch_bytes": 898919467,
+    "write_bytes": 94395328,
 }
 
 
