@@ -357,7 +357,9 @@ int moe_grouped_gemm_backward(const moe_gemm_backward_args* args, void* workspac
     p.seg_beg = seg;
     p.seg_end = seg + g.E;
     p.seg_c_stride = (int64_t)g.N * g.K;
-    e = moe::launch_grouped_gemm(p, 128, s);
+    // 256-row tiles where dw has rows enough (half the bytes per flop of the
+    // 128-row tile: the axolotl table's four shapes 3-16 % faster)
+    e = moe::launch_grouped_gemm(p, g.N >= 1024 ? 256 : 128, s);
     if (e != hipSuccess) return hip_status(e);
   }
   return MOE_OK;

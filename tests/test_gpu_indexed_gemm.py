@@ -177,10 +177,13 @@ BWD_SMALL = SMALL + [
     W.small_gemm_scenario("cg_bwd_g6_uneven", G=6, M=900, N=264, K=136,
                           sizes=(0, 400, 1, 250, 0, 249), block_m=64),
     W.small_gemm_scenario("cg_bwd_empty_rows", G=3, M=0, N=64, K=64, sizes=(0, 0, 0)),
-    # 16 x 8 weight-gradient tiles per expert, 512 in all: the persistent grid
-    # runs tile sequences whose K (the expert's padded rows: 0, 1024, 128,
-    # 1536) changes from tile to tile
-    W.small_gemm_scenario("cg_bwd_persistent", G=4, M=2400, N=2048, K=2048,
+    # 512 weight-gradient tiles on the persistent grid, whose tile sequences
+    # change K (the expert's padded rows: 0, 1024, 128, 1536) from tile to
+    # tile: 256-row tiles (N >= 1024; 8 x 16 per expert) and 128-row tiles
+    # (8 x 16 per expert)
+    W.small_gemm_scenario("cg_bwd_persistent", G=4, M=2400, N=2048, K=4096,
+                          sizes=(0, 900, 1, 1499)),
+    W.small_gemm_scenario("cg_bwd_persistent_128", G=4, M=2400, N=1000, K=4096,
                           sizes=(0, 900, 1, 1499)),
 ]
 
