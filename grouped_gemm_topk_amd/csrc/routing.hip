@@ -174,15 +174,16 @@ __device__ void align_offsets(const int* s_cnt, int* s_off, int E, int bm, int* 
 }
 
 // expert_ids of every block, the pad entries of sorted_ids (value n) and the
-// padded total, all threads of the workgroup in parallel.
+// padded total.  Worker w of nw (a thread index over every workgroup that
+// takes part) writes entries w, w + nw, ...; worker 0 writes the total.
 __device__ void write_layout(const int* s_cnt, const int* s_off, int E, int bm, int n, int total,
-                             int* sorted_ids, int* expert_ids, int* ntpp) {
-  const int tid = threadIdx.x;
+                             int* sorted_ids, int* expert_ids, int* ntpp, int w, int nw) {
+  const int tid = w;
   if (tid == 0) *ntpp = total;
   // expert of a block: the last expert whose offset is <= the block start (an
   // empty expert shares its offset with the next one, so the last such expert
   // is the non-empty one that owns the block)
-  for (int b = tid; b * bm < total; b += blockDim.x) {
+  for (int b = tid; b * bm < total; b += nw) {
     const int pos = b * bm;
     int lo = 0, hi = E - 1;
     while (lo < hi) {
@@ -192,7 +193,7 @@ __device__ void write_layout(const int* s_cnt, const int* s_off, int E, int bm, 
     expert_ids[b] = lo;
   }
   // pads: expert e owns padded positions [off + c, off + round_up(c, bm))
-  for (int idx = tid; idx < E * bm; idx += blockDim.x) {
+  for (int idx = tid; idx < E * bm; idx += nw) {
     const int e = idx / bm, r = idx - e * bm;
     const int c = s_cnt[e];
     const int pc = (c + bm - 1) / bm * bm;
@@ -468,7 +469,8 @@ __global__ void __launch_bounds__(1024) align_single_kernel(AlignParams a, GateP
   __syncthreads();
   align_offsets(s_cnt, s_off, a.E, a.block_m, &s_total);
   __syncthreads();
-  write_layout(s_cnt, s_off, a.E, a.block_m, a.n, s_total, a.sorted_ids, a.expert_ids, a.ntpp);
+  write_layout(s_cnt, s_off, a.E, a.block_m, a.n, s_total, a.sorted_ids, a.expert_ids, a.ntpp,
+               tid, blockDim.x);
   for (int e = tid; e < a.E; e += blockDim.x) s_cursor[e] = s_off[e];
   __syncthreads();
   stable_scatter([&](int i) { return s_ids[i]; }, 0, a.n, a.E, s_cursor, s_wcnt, s_base,
@@ -499,9 +501,9 @@ __global__ void __launch_bounds__(1024) align_count_kernel(AlignParams a) {
 }
 
 // Step 2: every workgroup derives the expert offsets and its chunk's base per
-// expert from all chunk histograms (a few KB from L2), workgroup 0 writes the
-// layout (expert_ids, pads, padded total), and each workgroup scatters its
-// chunk's slots stably.
+// expert from all chunk histograms (a few KB from L2), the workgroups write
+// the layout (expert_ids, pads, padded total) together, and each workgroup
+// scatters its chunk's slots stably.
 __global__ void __launch_bounds__(1024) align_place_kernel(AlignParams a) {
   __shared__ int s_tot[4][256], s_pre[4][256];
   __shared__ int s_cnt[256], s_off[256], s_cursor[256];
@@ -513,6 +515,9 @@ __global__ void __launch_bounds__(1024) align_place_kernel(AlignParams a) {
   {
     int tot = 0, pre = 0;
     if (e < a.E) {
+      // (unrolled so that the loads, from L2, are in flight together: at
+      // 64 chunks each thread reads 16)
+#pragma unroll 16
       for (int b = q; b < a.nblocks; b += 4) {
         const int c = a.block_counts[b * a.E + e];
         tot += c;
@@ -530,8 +535,9 @@ __global__ void __launch_bounds__(1024) align_place_kernel(AlignParams a) {
   __syncthreads();
   align_offsets(s_cnt, s_off, a.E, a.block_m, &s_total);
   __syncthreads();
-  if (blockIdx.x == 0)
-    write_layout(s_cnt, s_off, a.E, a.block_m, a.n, s_total, a.sorted_ids, a.expert_ids, a.ntpp);
+  // every workgroup has the layout: they write its block ids and pads together
+  write_layout(s_cnt, s_off, a.E, a.block_m, a.n, s_total, a.sorted_ids, a.expert_ids, a.ntpp,
+               (int)(blockIdx.x * blockDim.x + tid), (int)(gridDim.x * blockDim.x));
   for (int x = tid; x < a.E; x += blockDim.x) s_cursor[x] = s_off[x] + s_pre[0][x];
   __syncthreads();
   const int64_t s0 = (int64_t)blockIdx.x * a.chunk;
