@@ -34,6 +34,14 @@ CASES = [
                                           topk_group=4, n_shared=1, block_m=128), True),
     ("prefill_softmax_small", W.small_config("prefill_softmax_small", T=333, H=128, I=96,
                                              E=8, top_k=2, block_m=64), True),
+    # the persistent 128-row grid (loader / compute split), several tiles per
+    # workgroup in both GEMMs
+    ("prefill_persistent_128", W.small_config("prefill_persistent_128", T=16384, H=104, I=520,
+                                              E=4, top_k=2, block_m=128), True),
+    # 256-row tiles whose last rounds (24 of 280 tiles in each GEMM on 256
+    # CUs) run in the slice launch
+    ("prefill_split_256", W.small_config("prefill_split_256", T=8600, H=1000, I=504, E=4,
+                                         top_k=2, block_m=256), True),
 ]
 
 
