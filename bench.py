@@ -57,7 +57,7 @@ DOMINANT_TRAFFIC = {
     "src": "grouped_gemm_topk_amd/csrc/gemm.hip",
     "sha256": "f0864f546a521352fd6cf2f7d6be1d2d7d13dd2cb26c9546492390a0efef5d86",
     "config": "dsv3",
-    # one call: the persistent launch and its (here empty) last-round slice launch
+    # one call, one persistent launch
     "fetch_bytes": 898913152,
     "write_bytes": 95189365,
 }

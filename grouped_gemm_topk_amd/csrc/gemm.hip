@@ -161,10 +161,18 @@ constexpr int kEidsLds = BM >= 128 ? 2048 : 0;
 // WNT: weight rows are loaded with the non-temporal hint (see launch_bm).
 // PC: MOE_NLW more waves (loader waves) issue every direct load and the
 // WAVES_M x WAVES_N waves only compute and store (see the PC branch below).
-template <int BM, int BNW, int WAVES_M, int WAVES_N, bool SW, int BK, int NS, int MINW,
-          bool WNT = false, bool PC = false>
-__global__ void __launch_bounds__(64 * (WAVES_M * WAVES_N + (PC ? MOE_NLW : 0)), MINW)
-    grouped_gemm_kernel(GemmParams pin) {
+// LDS bytes of one tile configuration's body: its stages, the expert-id copy
+// and (loader / compute split) the sorted-id buffers of the loader waves
+template <int BM, int BNW, int BK, int NS, bool PC>
+constexpr int kBodyLds = NS * (BM + BNW) * (BK / 8) * 16 + kEidsLds<BM> * 4 + (PC ? 4 * BM * 4 : 0);
+
+// One tile configuration's work in a launch; the kernel below runs it once,
+// or (the 256 x 256 tile) twice.  tail_mode: 0 all tiles of the launch, 1 its
+// full rounds, 2 the slices of its last round (see nrun); lds: the
+// workgroup's LDS, kBodyLds bytes of it used.
+template <int BM, int BNW, int WAVES_M, int WAVES_N, bool SW, int BK, int NS, bool WNT, bool PC>
+__device__ __forceinline__ void gemm_body(const GemmParams& pin, const int tail_mode,
+                                          unsigned char* lds) {
   constexpr int NCW = WAVES_M * WAVES_N;        // compute waves
   constexpr int NT = 64 * (NCW + (PC ? MOE_NLW : 0));   // threads of the workgroup
   constexpr int LT = PC ? 64 * MOE_NLW : NT;            // threads that issue direct loads
@@ -186,8 +194,11 @@ __global__ void __launch_bounds__(64 * (WAVES_M * WAVES_N + (PC ? MOE_NLW : 0)),
   // LDS stages (loads run NS - 1 K steps ahead)
   constexpr int NBUF = NS;
   static_assert(NS >= 2, "the load pipeline needs two or more stages");
-  __shared__ u32x4 sX[NBUF][BM * CPR];
-  __shared__ u32x4 sW[NBUF][BNW * CPR];
+  typedef u32x4 XStage[BM * CPR];
+  typedef u32x4 WStage[BNW * CPR];
+  XStage* const sX = reinterpret_cast<XStage*>(lds);
+  WStage* const sW = reinterpret_cast<WStage*>(lds + NBUF * BM * CPR * 16);
+  unsigned char* const lds_rest = lds + NBUF * (BM + BNW) * CPR * 16;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -219,20 +230,21 @@ __global__ void __launch_bounds__(64 * (WAVES_M * WAVES_N + (PC ? MOE_NLW : 0)),
     vbr = min(pin.mblocks, ((pin.ntpp ? *pin.ntpp : pin.M) + BM - 1) / BM);
     nvalid = ntn * (vbr + pin.nsb);
   }
-  // nrun: the launch-sequence indices this launch runs.  A persistent launch
-  // whose last round would fill at most a quarter of the grid stops after its
-  // full rounds (tail 1); a second launch (tail 2) runs the tiles of that
-  // round cut into tail_s slices of its own, narrower tile width, one per
-  // workgroup, so that the last round's few tiles are spread over the CUs.
+  // nrun: the launch-sequence indices this pass runs.  In a persistent
+  // launch whose last round would fill at most a quarter of the grid, the
+  // pass over the full tiles stops after its full rounds (tail mode 1), and
+  // a second pass (tail mode 2, see grouped_gemm_kernel) runs the tiles of
+  // that round cut into tail_s slices of its own, narrower tile width, one
+  // per workgroup, so that the last round's few tiles are spread over the CUs.
   // (A quarter: the slices then fit in one round.  On the dsv3 layer's W2, a
   // last round of 44 tiles took 72 us and its 176 slices take 43 us; two
   // rounds of slices would cost about what a half-full last round does.)
   int nrun = nvalid, tail_base = 0;
-  if (pin.tail) {
+  if (tail_mode) {
     const int gm = pin.main_grid;
     const int rem = nvalid % gm;
     const bool split = nvalid > gm && rem > 0 && 4 * rem <= gm;
-    if (pin.tail == 1) {
+    if (tail_mode == 1) {
       if (split) nrun = nvalid - rem;
     } else {
       if (!split) return;
@@ -256,10 +268,7 @@ __global__ void __launch_bounds__(64 * (WAVES_M * WAVES_N + (PC ? MOE_NLW : 0)),
   // (every tile's mapping reads them) when the tile's LDS leaves room
   typedef __attribute__((address_space(3))) int lds_int;
   lds_int* s_eids = nullptr;
-  if constexpr (kEidsLds<BM> > 0) {
-    __shared__ int s_eids_buf[kEidsLds<BM> > 0 ? kEidsLds<BM> : 1];
-    s_eids = (lds_int*)s_eids_buf;
-  }
+  if constexpr (kEidsLds<BM> > 0) s_eids = (lds_int*)lds_rest;
   const bool eids_lds = kEidsLds<BM> > 0 && pin.nseg == 0 && pin.expert_ids && vbr <= kEidsLds<BM>;
   if (eids_lds) {
     for (int i = tid; i < vbr; i += NT) s_eids[i] = pin.expert_ids[i];
@@ -273,7 +282,7 @@ __global__ void __launch_bounds__(64 * (WAVES_M * WAVES_N + (PC ? MOE_NLW : 0)),
   // a tile's place: m-block, n-tile, expert (the segment in segmented launches)
   struct Map {
     int mb, nt, e;
-    int slice;            // slice of the n-tile (slice launches)
+    int slice;            // slice of the n-tile (tail mode 2)
     bool second, store;   // dense second part; false only for an invalid expert id
   };
   auto resolve = [&](int Lt) -> Map {
@@ -281,8 +290,8 @@ __global__ void __launch_bounds__(64 * (WAVES_M * WAVES_N + (PC ? MOE_NLW : 0)),
     m.store = true;
     m.second = false;
     m.slice = 0;
-    if (pin.tail == 2) {
-      // a slice of a tile of the main launch's last round.  Workgroup Lt runs
+    if (tail_mode == 2) {
+      // a slice of a tile of the last round.  Workgroup Lt runs
       // on XCD Lt mod 8: it takes a tile whose launch index is numbered for
       // that XCD (index tail_base + j with j = Lt - tail_base mod 8), so that
       // the slices of one tile, which read the same token rows, and the
@@ -340,8 +349,8 @@ __global__ void __launch_bounds__(64 * (WAVES_M * WAVES_N + (PC ? MOE_NLW : 0)),
     Tile t;
     t.store = m.store;
     t.m0 = m.mb * BM;
-    t.n0 = pin.tail == 2 ? m.nt * pin.main_tile_n + m.slice * (SW ? BNW / 2 : BNW)
-                         : m.nt * (SW ? BNW / 2 : BNW);
+    t.n0 = tail_mode == 2 ? m.nt * pin.main_tile_n + m.slice * (SW ? BNW / 2 : BNW)
+                          : m.nt * (SW ? BNW / 2 : BNW);
     t.K = pin.K;
     if (pin.nseg > 0) {
       const int beg = pin.seg_beg[m.e];
@@ -720,7 +729,7 @@ __global__ void __launch_bounds__(64 * (WAVES_M * WAVES_N + (PC ? MOE_NLW : 0)),
     // after the write, and R >= J keeps a buffer from being rewritten before
     // it was read
     constexpr int R = 4;
-    __shared__ int s_ids[R][BM];
+    int (*const s_ids)[BM] = reinterpret_cast<int (*)[BM]>(lds_rest + kEidsLds<BM> * 4);
     const int L0 = blockIdx.x;
     const int ntl = (nrun - L0 + G - 1) / G;   // tiles of this workgroup (>= 1)
     const int nk = (K + BK - 1) / BK;
@@ -942,6 +951,30 @@ __global__ void __launch_bounds__(64 * (WAVES_M * WAVES_N + (PC ? MOE_NLW : 0)),
 #undef MOE_VMW
 }
 
+// The grouped GEMM kernel: one tile configuration's work (gemm_body).  A
+// persistent 256 x 256 launch whose last round would fill at most a quarter
+// of the grid runs its full rounds and then, in the same launch, the tiles of
+// that round cut into slices of 64 weight rows (32 act columns with SwiGLU)
+// on eight waves of 32-row MFMA blocks, so every output is the same bit for
+// bit as with the whole tiles; a workgroup takes its slice as soon as its
+// full rounds are done.
+template <int BM, int BNW, int WAVES_M, int WAVES_N, bool SW, int BK, int NS, int MINW,
+          bool WNT = false, bool PC = false>
+__global__ void __launch_bounds__(64 * (WAVES_M * WAVES_N + (PC ? MOE_NLW : 0)), MINW)
+    grouped_gemm_kernel(GemmParams pin) {
+  constexpr bool SLICES = BM == 256 && BNW == 256 && !PC && WAVES_M * WAVES_N == 8;
+  constexpr int MAIN_LDS = kBodyLds<BM, BNW, BK, NS, PC>;
+  constexpr int SLICE_LDS = SLICES ? kBodyLds<BM, 64, BK, 3, false> : 0;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[MAIN_LDS > SLICE_LDS ? MAIN_LDS : SLICE_LDS];
+  gemm_body<BM, BNW, WAVES_M, WAVES_N, SW, BK, NS, WNT, PC>(pin, pin.tail, lds);
+  if constexpr (SLICES) {
+    if (pin.tail == 1) {
+      __syncthreads();   // every wave is done with the stages of its last tile
+      gemm_body<BM, 64, BM / 32, 1, SW, BK, 3, false, false>(pin, 2, lds);
+    }
+  }
+}
+
 // compute units of the current device (cached per device, safe to call from
 // several host threads; 0 if unknown)
 int cu_count() {
@@ -1021,11 +1054,15 @@ hipError_t launch_bm(GemmParams p, hipStream_t s) {
       persistent = true;
     }
   }
-  // (the last-round split pays with 256-row tiles only: dsv3 layer
-  // 1083 -> 1058 us; with 128-row tiles the main launch's last round is
-  // short and overlaps the tile before it, and the split costs 2-3 %)
-  p.tail = persistent && BM == 256 && p.nseg == 0 ? 1 : 0;
+  // The last-round slices (see grouped_gemm_kernel) pay with 256-row tiles
+  // only: with 128-row tiles the main launch's last round is short and
+  // overlaps the tile before it, and the split cost 2-3 %.  The grid is a
+  // multiple of 32: the last round's at most nwg / 4 tiles, at most nwg / 32
+  // per XCD, each in tail_s slices on its XCD's nwg / 8 workgroups.
+  p.tail = persistent && BM == 256 && p.nseg == 0 && nwg % 32 == 0 ? 1 : 0;
   p.main_grid = (int)nwg;
+  p.main_tile_n = tile_n;
+  p.tail_s = tile_n / (sw ? 32 : 64);   // slices of 64 weight rows
   // Experts that hold on average at most one m-block (T * top_k <= E * BM)
   // use each weight tile in one tile only: with no dense second part (whose
   // weights every m-block reads), the 128-row tile then streams its weight
@@ -1035,32 +1072,7 @@ hipError_t launch_bm(GemmParams p, hipStream_t s) {
   const bool wnt = BM == 128 && p.nseg == 0 && p.M2 == 0 && p.expert_ids &&
                    (int64_t)p.num_valid <= (int64_t)p.E * BM;
   const dim3 grid((unsigned)nwg), block(64 * WAVES_M * WAVES_N);
-  hipError_t e = launch_main<BM, BNW, WAVES_M, WAVES_N, BK, NS, MINW>(p, grid, block, sw, wnt, s);
-  if (e != hipSuccess || !p.tail) return e;
-  // the slices of a last round filling at most a quarter of the grid (each kernel
-  // decides from the tile count; with no such round the slice launch's
-  // workgroups return at once): eight waves of 32-row MFMA blocks, as in
-  // the main launch, so every output is the same bit for bit, in 64-column
-  // slices (32 act columns with SwiGLU)
-  if constexpr (BM == 256) {
-    constexpr int TWM = BM / 32, TWN = 1;   // one wave per 32-row block
-    constexpr int TB_SW = 64, TB = 64;      // slice tile widths in weight rows
-    GemmParams pt = p;
-    pt.tail = 2;
-    pt.main_tile_n = tile_n;
-    pt.tail_s = tile_n / (sw ? TB_SW / 2 : TB);
-    // the last round holds at most nwg / 4 tiles, at most ceil(nwg / 32) per
-    // XCD, each in tail_s slices on its XCD's workgroups
-    const dim3 tgrid((unsigned)(8 * ((nwg + 31) / 32) * pt.tail_s)), tblock(64 * 8);
-    if (sw)
-      hipLaunchKernelGGL((grouped_gemm_kernel<BM, TB_SW, TWM, TWN, true, BK, 3, 1>), tgrid, tblock, 0,
-                         s, pt);
-    else
-      hipLaunchKernelGGL((grouped_gemm_kernel<BM, TB, TWM, TWN, false, BK, 3, 1>), tgrid, tblock, 0, s,
-                         pt);
-    return hipGetLastError();
-  }
-  return hipSuccess;
+  return launch_main<BM, BNW, WAVES_M, WAVES_N, BK, NS, MINW>(p, grid, block, sw, wnt, s);
 }
 
 }  // namespace

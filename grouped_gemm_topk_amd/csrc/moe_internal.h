@@ -88,11 +88,10 @@ struct GemmParams {
   // one workgroup per tile instead of the persistent grid of the 128- and
   // 256-row tiles (same results; for comparisons)
   int per_tile;
-  // set by the launcher: 1 in a persistent launch (which then leaves a last
-  // round filling at most half its grid to a second launch), 2 in that second
-  // launch, which cuts each of those tiles into tail_s slices of its own tile
-  // width; main_grid = the persistent launch's grid, main_tile_n = its tile
-  // width in output columns
+  // set by the launcher: 1 in a persistent 256-row launch, which then runs a
+  // last round filling at most a quarter of its grid with each of those tiles
+  // cut into tail_s slices; main_grid = the persistent grid, main_tile_n =
+  // the tile width in output columns
   int tail, tail_s, main_grid, main_tile_n;
 };
 

@@ -64,10 +64,9 @@ enum { MOE_EPI_STORE = 0, MOE_EPI_SWIGLU = 1, MOE_EPI_RELU2 = 2, MOE_EPI_WEIGHTE
  * BLOCK_M 128 and 256 one workgroup per compute unit runs a sequence of tiles
  * (PERSISTENT, the default), or one workgroup per tile (PER_TILE; the
  * axolotl page's benchmark times its persistent and its non-persistent
- * kernels side by side).  A persistent call at BLOCK_M 256 is two kernel
- * launches on the stream: when the last round of tiles fills at most a
- * quarter of the grid, the second launch runs those tiles in narrower
- * slices (otherwise its workgroups return at once). */
+ * kernels side by side).  At BLOCK_M 256 the persistent launch runs a last
+ * round of tiles that fills at most a quarter of the grid in narrower slices
+ * (same results), one per workgroup as its full rounds end. */
 enum { MOE_SCHED_PERSISTENT = 0, MOE_SCHED_PER_TILE = 1 };
 
 /* Limits enforced by validation. */

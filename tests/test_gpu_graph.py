@@ -39,7 +39,7 @@ CASES = [
     ("prefill_persistent_128", W.small_config("prefill_persistent_128", T=16384, H=104, I=520,
                                               E=4, top_k=2, block_m=128), True),
     # 256-row tiles whose last rounds (24 of 280 tiles in each GEMM on 256
-    # CUs) run in the slice launch
+    # CUs) run in 64-column slices
     ("prefill_split_256", W.small_config("prefill_split_256", T=8600, H=1000, I=504, E=4,
                                          top_k=2, block_m=256), True),
 ]

@@ -93,7 +93,7 @@ SCHED = [
     W.small_gemm_scenario("sched_bm128", G=6, M=6 * 4000, N=520, K=264, block_m=128),
     W.small_gemm_scenario("sched_bm256", G=5, M=5 * 6000, N=1000, K=200, block_m=256),
     # 80 m-blocks x 4 n-tiles = 320 tiles: on 256 CUs the last round's 64
-    # tiles run in 64-column slices of a second launch
+    # tiles run in 64-column slices
     W.small_gemm_scenario("sched_bm256_split", G=5, M=5 * 3900, N=1000, K=200, block_m=256),
     W.small_gemm_scenario("sched_bm64", G=8, M=8 * 70, N=136, K=264, block_m=64),
 ]

@@ -11,8 +11,8 @@
 - two K steps per tile (with the loader waves of the 128-row tile, a tile's
   sorted ids are read three tiles after they are written).
 - with 256-row tiles, a last round that fills at most a quarter of the
-  grid: the persistent launch stops after its full rounds and a second
-  launch runs that round's tiles in 64-column slices (both GEMMs, ragged K,
+  grid: each workgroup runs its full rounds and then one of that round's
+  tiles' 64-column slices (both GEMMs, ragged K,
   the shared expert's dense tiles in the sliced round, and a layer whose
   W13 launch keeps a last round of half the grid while its W2 launch
   splits).

@@ -66,7 +66,7 @@ PAIRS = [
     # prefill, then decode on the scratch it left
     (W.CONFIGS["tiny"], W.small_config("na_decode_t3", T=3, H=256, I=512, E=8, top_k=2)),
     # 256-row tiles: a W13 launch of 8 x 40 = 320 tiles on the persistent grid
-    # whose last round of 64 runs in the slice launch, then half the tokens
+    # whose last round of 64 runs in 64-column slices, then half the tokens
     (W.small_config("na_split_256", T=2048, H=256, I=5120, E=1, top_k=1, block_m=256),
      W.small_config("na_half_256", T=1024, H=256, I=5120, E=1, top_k=1, block_m=256)),
 ]
