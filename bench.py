@@ -55,11 +55,11 @@ DOMINANT_KERNEL = {
 
 DOMINANT_TRAFFIC = {
     "src": "grouped_gemm_topk_amd/csrc/gemm.hip",
-    "sha256": "f0864f546a521352fd6cf2f7d6be1d2d7d13dd2cb26c9546492390a0efef5d86",
+    "sha256": "f881d4cceaa2b99c709e9ec8acb7b5ef2bf3c795bd442b4d3a2fa1f51faaadc5",
     "config": "dsv3",
     # one call, one persistent launch
-    "fetch_bytes": 898913152,
-    "write_bytes": 95189365,
+    "fetch_bytes": 898884459,
+    "write_bytes": 95251957,
 }
 
 
