@@ -55,11 +55,11 @@ DOMINANT_KERNEL = {
 
 DOMINANT_TRAFFIC = {
     "src": "grouped_gemm_topk_amd/csrc/gemm.hip",
-    "sha256": "f881d4cceaa2b99c709e9ec8acb7b5ef2bf3c795bd442b4d3a2fa1f51faaadc5",
+    "sha256": "b5d922985dcb8baad466192d8ad6824bea27542d557be1d540dbdfd58450dc9f",
     "config": "dsv3",
     # one call, one persistent launch
-    "fetch_bytes": 898884459,
-    "write_bytes": 95251957,
+    "fetch_bytes": 898884203,
+    "write_bytes": 95288517,
 }
 
 
